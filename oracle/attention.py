@@ -1,0 +1,208 @@
+"""Float64 CPU oracle for the exact attention forward -- test infrastructure.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline
+leg may import this module.  It is deliberately the plain definition: the
+score matrix S and the probabilities P are materialised for a whole head, with
+no blocking, fusion or reordering beyond what the pages state.
+
+Conventions (the pages leave these open; the readings taken are listed in the
+design notes):
+
+* Layout: q is (..., T_q, d), k and v are (..., T_kv, d); all leading axes are
+  independent (batch, head) slices.
+* ``scale`` multiplies q.k; the pages use 1/sqrt(d).
+* Causal: key j is visible to query i iff j <= i + (T_kv - T_q).  For
+  self-attention (T_q == T_kv) this is "position i sees the keys up to and
+  including itself", which gives the T(T+1)/2 pair count of "Attention and
+  Its Computational Cost", section "What is being computed".  Causal with
+  T_q > T_kv would leave rows with no keys and is rejected.
+* LSE is the natural-log normaliser of each row in units of the scaled score:
+  lse_i = m_i + ln(l_i) = ln sum_j exp(scale * q_i . k_j).
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def _as_f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def attention(q, k, v, scale: float, causal: bool = False, rows=None):
+    """The definition, materialised.
+
+    "FlashAttention IO-aware tiling lab", kernel-phase captions: S = QK^T /
+    sqrt(d), P = softmax(S), O = PV.  "Attention and Its Computational Cost",
+    "What is being computed": S and P are both T_q x T_kv; causal
+    self-attention keeps T(T+1)/2 of the pairs.
+
+    Steps, per leading slice:
+      1. S = (Q K^T) * scale                         (T_q x T_kv)
+      2. causal: S[i, j] = -inf where j > i + T_kv - T_q
+      3. m_i = max_j S[i, j];  P = exp(S - m);  l_i = sum_j P[i, j]
+      4. O = (P V) / l;  lse_i = m_i + ln l_i
+
+    ``rows`` (optional, 1-D int array) restricts the computation to those query
+    rows of the full T_q-row problem; the causal mask still uses each row's
+    absolute index, so the result equals the same rows of the full answer.
+
+    Returns (o, lse) as float64 arrays of shape (..., R, d_v) and (..., R),
+    where R is T_q or len(rows).
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    if q.ndim < 2 or k.ndim != q.ndim or v.ndim != q.ndim:
+        raise ValueError("q, k, v must have the same rank >= 2")
+    tq, d = q.shape[-2], q.shape[-1]
+    tkv = k.shape[-2]
+    if k.shape[-1] != d or v.shape[-2] != tkv or k.shape[:-2] != q.shape[:-2] or v.shape[:-2] != q.shape[:-2]:
+        raise ValueError("shape mismatch between q, k, v")
+    if tq < 1 or tkv < 1 or d < 1:
+        raise ValueError("sizes must be >= 1")
+    if causal and tq > tkv:
+        raise ValueError("causal attention needs T_q <= T_kv (every row must see a key)")
+    row_idx = np.arange(tq) if rows is None else np.asarray(rows, dtype=np.int64)
+    lead = q.shape[:-2]
+    dv = v.shape[-1]
+    qf = q.reshape((-1, tq, d))
+    kf = k.reshape((-1, tkv, d))
+    vf = v.reshape((-1, tkv, dv))
+    n = qf.shape[0]
+    o_out = np.empty((n, row_idx.size, dv))
+    lse_out = np.empty((n, row_idx.size))
+    if causal:
+        # visible[i, j] is True iff key j may be seen by query row_idx[i]
+        visible = np.arange(tkv)[None, :] <= (row_idx[:, None] + (tkv - tq))
+    for s in range(n):
+        scores = qf[s, row_idx] @ kf[s].T          # step 1 (unscaled product)
+        scores *= scale
+        if causal:                                  # step 2
+            scores[~visible] = -np.inf
+        m = scores.max(axis=1)                      # step 3
+        np.subtract(scores, m[:, None], out=scores)
+        np.exp(scores, out=scores)                  # scores now holds P
+        l = scores.sum(axis=1)
+        o_out[s] = (scores @ vf[s]) / l[:, None]    # step 4
+        lse_out[s] = m + np.log(l)
+    return o_out.reshape(lead + (row_idx.size, dv)), lse_out.reshape(lead + (row_idx.size,))
+
+
+def standard_attention(q, K, V):
+    """One query against a full key set, score vector materialised.
+
+    "E8.1 IO-aware attention", "Do it in code": softmax(K q / sqrt(d)) V for a
+    single query.  Returns the d_v-vector output.
+    """
+    q = _as_f64(q)
+    K = _as_f64(K)
+    V = _as_f64(V)
+    s = (K @ q) / math.sqrt(q.shape[0])
+    p = np.exp(s - s.max())
+    return (p @ V) / p.sum()
+
+
+def online_softmax_states(scores, block: int):
+    """Running (m, l) after each block of a score row.
+
+    "IO-Aware Attention: Tiling the Score Matrix Without Materializing It",
+    section "Softmax over blocks, exactly", the recurrence for m_i and l_i:
+    the new maximum is the max of the old one and the block's maximum; the old
+    sum is multiplied by exp(m_old - m_new) before the block's terms
+    exp(s_j - m_new) are added.  Start: m = -inf, l = 0.
+
+    Returns a list of (m, l) pairs, one per block, in block order.
+    """
+    if block < 1:
+        raise ValueError("block must be at least 1")
+    s = _as_f64(scores).ravel()
+    m, l = -math.inf, 0.0
+    states = []
+    for start in range(0, s.size, block):
+        sb = s[start:start + block]
+        m_new = max(m, float(sb.max()))
+        l = l * math.exp(m - m_new) + float(np.exp(sb - m_new).sum())
+        m = m_new
+        states.append((m, l))
+    return states
+
+
+def online_attention(q, K, V, block: int):
+    """The blockwise online form for one query, never holding more than one
+    block of scores.
+
+    "E8.1 IO-aware attention", "Do it in code" (block must be >= 1, otherwise
+    ValueError), with the recurrence of "IO-Aware Attention: Tiling the Score
+    Matrix Without Materializing It", section "Softmax over blocks, exactly":
+    per block, new_m = max(m, block max); rescale the running sum and the
+    running weighted value sum by exp(m - new_m); add the block's
+    exp(score - new_m) terms; divide once at the end.
+    """
+    if block < 1:
+        raise ValueError("block must be at least 1")
+    q = _as_f64(q)
+    K = _as_f64(K)
+    V = _as_f64(V)
+    n = K.shape[0]
+    scale = 1.0 / math.sqrt(q.shape[0])
+    m, l = -math.inf, 0.0
+    acc = np.zeros(V.shape[1])
+    for start in range(0, n, block):
+        s = (K[start:start + block] @ q) * scale
+        m_new = max(m, float(s.max()))
+        r = math.exp(m - m_new)
+        e = np.exp(s - m_new)
+        l = l * r + float(e.sum())
+        acc = acc * r + e @ V[start:start + block]
+        m = m_new
+    return acc / l
+
+
+def combine_partials(o_parts, lse_parts):
+    """Merge per-partition results with the softmax rescaling.
+
+    "IO-Aware Attention: Tiling the Score Matrix Without Materializing It",
+    section "Parallelism and the cost of the split": each key partition yields
+    a partial output and a partial normaliser, merged with the same rescaling
+    recurrence applied across partitions.  With partition p holding the
+    normalised output O_p and lse_p = ln(l_p) + m_p:
+        M = max_p lse_p,  w_p = exp(lse_p - M),
+        lse = M + ln(sum_p w_p),  O = sum_p w_p O_p / sum_p w_p.
+
+    o_parts: (P, ..., d_v), lse_parts: (P, ...).  Partitions with lse = -inf
+    (no keys) get zero weight.
+    """
+    o_parts = _as_f64(o_parts)
+    lse_parts = _as_f64(lse_parts)
+    M = lse_parts.max(axis=0)
+    w = np.exp(lse_parts - M[None])
+    wsum = w.sum(axis=0)
+    o = (w[..., None] * o_parts).sum(axis=0) / wsum[..., None]
+    return o, M + np.log(wsum)
+
+
+def split_attention(q, k, v, scale: float, num_splits: int):
+    """Non-causal attention over key partitions, then merged.
+
+    Partition p covers keys [floor(p T / P), floor((p + 1) T / P)); each one
+    is the plain definition (``attention``) on its keys, and the partials are
+    merged by ``combine_partials``.  Empty partitions (P > T) are skipped.
+    """
+    if num_splits < 1:
+        raise ValueError("num_splits must be at least 1")
+    k = _as_f64(k)
+    v = _as_f64(v)
+    tkv = k.shape[-2]
+    o_parts, lse_parts = [], []
+    for p in range(num_splits):
+        lo = (p * tkv) // num_splits
+        hi = ((p + 1) * tkv) // num_splits
+        if hi <= lo:
+            continue
+        o_p, lse_p = attention(q, k[..., lo:hi, :], v[..., lo:hi, :], scale)
+        o_parts.append(o_p)
+        lse_parts.append(lse_p)
+    return combine_partials(np.stack(o_parts), np.stack(lse_parts))

@@ -1,0 +1,446 @@
+"""Pins of the float64 oracle against what the pages and the mathematics fix.
+
+Nothing here touches a GPU or the HIP library.  Each check ties the oracle to
+something other than itself: the worked example printed on "E8.1 IO-aware
+attention", closed forms, invariants, special cases, brute force in plain
+Python loops on tiny inputs, and PyTorch's CPU attention in float64.
+
+``PIN_CHECKS`` below is also run against deliberately broken copies of the
+oracle (a dropped scale, transposed operands, a softmax over the wrong axis,
+a flipped causal mask, ...) to show that each plausible mistake is caught.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import attention
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+# ---------------------------------------------------------------- worked example
+
+def test_worked_example_after_block_1():
+    g = _load("online_softmax_worked_example.json")
+    states = oracle.online_softmax_states(g["scores"], g["block"])
+    m1, l1 = states[0]
+    assert m1 == g["after_block_1"]["m"]
+    half_ulp = 0.5 * 10 ** (-g["after_block_1"]["printed_decimals"])
+    assert abs(l1 - g["after_block_1"]["l"]) <= half_ulp
+
+
+def test_worked_example_final_state_equals_full_row():
+    g = _load("online_softmax_worked_example.json")
+    s = g["scores"]
+    m, l = oracle.online_softmax_states(s, g["block"])[-1]
+    assert m == max(s)
+    assert l == pytest.approx(math.fsum(math.exp(x - max(s)) for x in s), rel=1e-14)
+    # the same row as a d=1 attention problem: q=[1], k_j=[s_j], scale 1
+    q = np.ones((1, 1))
+    k = np.array(s, dtype=np.float64)[:, None]
+    v = np.eye(len(s))[:, :3]
+    _, lse = attention(q, k, v, scale=1.0)
+    assert lse[0] == pytest.approx(m + math.log(l), rel=1e-14)
+
+
+def test_worked_example_split_into_its_two_blocks():
+    """The two printed blocks merged by the cross-partition rescaling give the
+    full row (the split form of the same recurrence)."""
+    g = _load("online_softmax_worked_example.json")
+    s = np.array(g["scores"], dtype=np.float64)
+    q = np.ones((1, 1))
+    k = s[:, None]
+    rng = np.random.default_rng(7)
+    v = rng.standard_normal((len(s), 5))
+    o_full, lse_full = attention(q, k, v, 1.0)
+    o_split, lse_split = oracle.split_attention(q, k, v, 1.0, num_splits=2)
+    np.testing.assert_allclose(o_split, o_full, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse_split, lse_full, rtol=1e-14)
+    # block 1's normaliser is the printed state
+    m1, l1 = oracle.online_softmax_states(s, 4)[0]
+    _, lse_b1 = attention(q, k[:4], v[:4], 1.0)
+    assert lse_b1[0] == pytest.approx(m1 + math.log(l1), rel=1e-14)
+
+
+# ---------------------------------------------------------------- blockwise == full
+
+@pytest.mark.parametrize("n", [1, 2, 7, 17, 64])
+def test_blockwise_equals_full_for_every_block_size(n):
+    rng = np.random.default_rng(100 + n)
+    d, dv = 5, 4
+    q = _rand(rng, d)
+    K = 3.0 * _rand(rng, n, d)
+    V = _rand(rng, n, dv)
+    ref = oracle.standard_attention(q, K, V)
+    o_def, _ = attention(q[None], K, V, scale=1.0 / math.sqrt(d))
+    np.testing.assert_allclose(o_def[0], ref, rtol=1e-12, atol=1e-13)
+    for block in range(1, n + 1):
+        got = oracle.online_attention(q, K, V, block)
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+    s = (K @ q) / math.sqrt(d)
+    for block in range(1, n + 1):
+        m, l = oracle.online_softmax_states(s, block)[-1]
+        assert m == s.max()
+        assert l == pytest.approx(math.fsum(math.exp(x - s.max()) for x in s), rel=1e-12)
+
+
+@pytest.mark.parametrize("bad", [0, -1, -64])
+def test_block_below_one_raises(bad):
+    rng = np.random.default_rng(1)
+    with pytest.raises(ValueError):
+        oracle.online_attention(_rand(rng, 4), _rand(rng, 3, 4), _rand(rng, 3, 2), bad)
+    with pytest.raises(ValueError):
+        oracle.online_softmax_states([1.0, 2.0], bad)
+    with pytest.raises(ValueError):
+        oracle.num_blocks(10, bad)
+
+
+# ---------------------------------------------------------------- pin suite
+
+def _brute(q, k, v, scale, causal):
+    """The definition in plain Python loops (math.exp, fsum): no numpy
+    arithmetic, so it cannot share a mistake with the oracle's matmuls."""
+    q = np.asarray(q).tolist()
+    k = np.asarray(k).tolist()
+    v = np.asarray(v).tolist()
+    tq, tkv, dv = len(q), len(k), len(v[0])
+    o, lse = [], []
+    for i in range(tq):
+        s = []
+        for j in range(tkv):
+            if causal and j > i + (tkv - tq):
+                continue
+            s.append((j, scale * math.fsum(a * b for a, b in zip(q[i], k[j]))))
+        mx = max(x for _, x in s)
+        w = [(j, math.exp(x - mx)) for j, x in s]
+        den = math.fsum(x for _, x in w)
+        o.append([math.fsum(x * v[j][c] for j, x in w) / den for c in range(dv)])
+        lse.append(mx + math.log(den))
+    return np.array(o), np.array(lse)
+
+
+def _pin_tkv1(fn):
+    rng = np.random.default_rng(11)
+    q, k, v = _rand(rng, 6, 4), _rand(rng, 1, 4), _rand(rng, 1, 3)
+    o, lse = fn(q, k, v, 0.7, False)
+    ok = np.allclose(o, np.repeat(v, 6, axis=0), rtol=0, atol=1e-15)
+    return ok and np.allclose(lse, 0.7 * (q @ k[0]), rtol=1e-14, atol=1e-15)
+
+
+def _pin_zero_query(fn):
+    rng = np.random.default_rng(12)
+    q, k, v = np.zeros((3, 4)), _rand(rng, 9, 4), _rand(rng, 9, 5)
+    o, lse = fn(q, k, v, 0.5, False)
+    return np.allclose(o, v.mean(axis=0)[None], atol=1e-14) and np.allclose(lse, math.log(9), atol=1e-14)
+
+
+def _pin_ones_value(fn):
+    rng = np.random.default_rng(13)
+    q, k = _rand(rng, 5, 4), 2.0 * _rand(rng, 8, 4)
+    o, _ = fn(q, k, np.ones((8, 3)), 0.5, False)
+    o_c, _ = fn(q, k, np.ones((8, 3)), 0.5, True)
+    return np.allclose(o, 1.0, atol=1e-14) and np.allclose(o_c, 1.0, atol=1e-14)
+
+
+def _pin_causal_row0(fn):
+    rng = np.random.default_rng(14)
+    q, k, v = _rand(rng, 6, 4), _rand(rng, 6, 4), _rand(rng, 6, 3)
+    o, lse = fn(q, k, v, 0.5, True)
+    return np.allclose(o[0], v[0], atol=1e-15) and abs(lse[0] - 0.5 * q[0] @ k[0]) < 1e-14
+
+
+def _pin_two_keys(fn):
+    """T_kv = 2 has the closed form O = sigmoid(s0 - s1) v0 + sigmoid(s1 - s0) v1,
+    lse = max + log1p(exp(-|s0 - s1|))."""
+    rng = np.random.default_rng(15)
+    q, k, v = _rand(rng, 4, 3), _rand(rng, 2, 3), _rand(rng, 2, 2)
+    o, lse = fn(q, k, v, 0.9, False)
+    s0, s1 = 0.9 * (q @ k[0]), 0.9 * (q @ k[1])
+    a = 1.0 / (1.0 + np.exp(s1 - s0))
+    o_ref = a[:, None] * v[0][None] + (1 - a)[:, None] * v[1][None]
+    lse_ref = np.maximum(s0, s1) + np.log1p(np.exp(-np.abs(s0 - s1)))
+    return np.allclose(o, o_ref, atol=1e-14) and np.allclose(lse, lse_ref, atol=1e-14)
+
+
+def _pin_key_shift(fn):
+    """Adding u to every key shifts row i's scores by scale*q_i.u: O is
+    unchanged and lse moves by exactly that amount (softmax is per query row)."""
+    rng = np.random.default_rng(16)
+    q, k, v = _rand(rng, 5, 4), _rand(rng, 7, 4), _rand(rng, 7, 3)
+    u = 4.0 * _rand(rng, 4)
+    o1, l1 = fn(q, k, v, 0.6, False)
+    o2, l2 = fn(q, k + u[None], v, 0.6, False)
+    return np.allclose(o1, o2, atol=1e-12) and np.allclose(l2 - l1, 0.6 * (q @ u), atol=1e-12)
+
+
+def _pin_permutation(fn):
+    rng = np.random.default_rng(17)
+    q, k, v = _rand(rng, 5, 4), _rand(rng, 9, 4), _rand(rng, 9, 3)
+    perm = rng.permutation(9)
+    o1, l1 = fn(q, k, v, 0.4, False)
+    o2, l2 = fn(q, k[perm], v[perm], 0.4, False)
+    return np.allclose(o1, o2, atol=1e-14) and np.allclose(l1, l2, atol=1e-14)
+
+
+def _pin_brute(fn):
+    rng = np.random.default_rng(18)
+    ok = True
+    for tq, tkv, causal in [(5, 5, False), (5, 5, True), (3, 7, True), (4, 6, False), (1, 6, True)]:
+        q, k, v = _rand(rng, tq, 3), 2 * _rand(rng, tkv, 3), _rand(rng, tkv, 2)
+        o, lse = fn(q, k, v, 0.8, causal)
+        ob, lb = _brute(q, k, v, 0.8, causal)
+        ok = ok and np.allclose(o, ob, rtol=1e-13, atol=1e-14) and np.allclose(lse, lb, rtol=1e-13, atol=1e-14)
+    return ok
+
+
+def _pin_torch_sdpa(fn):
+    """Library cross-check: PyTorch's CPU attention in float64 (top-left
+    causal alignment, which equals ours when T_q == T_kv)."""
+    rng = np.random.default_rng(19)
+    ok = True
+    for causal in (False, True):
+        q, k, v = _rand(rng, 16, 8), _rand(rng, 16, 8), _rand(rng, 16, 8)
+        o, _ = fn(q, k, v, 0.3, causal)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q)[None, None], torch.from_numpy(k)[None, None],
+            torch.from_numpy(v)[None, None], is_causal=causal, scale=0.3)[0, 0].numpy()
+        ok = ok and np.allclose(o, ref, rtol=1e-12, atol=1e-13)
+    return ok
+
+
+def _pin_causal_suffix(fn):
+    """Bottom-right causal: the last T_q rows of a T x T causal problem are the
+    T_q-query causal problem over the same keys (one new query sees every
+    cached key), and T_q = 1 causal is plain attention over all keys."""
+    rng = np.random.default_rng(20)
+    qf, k, v = _rand(rng, 9, 4), _rand(rng, 9, 4), _rand(rng, 9, 3)
+    of, lf = fn(qf, k, v, 0.5, True)
+    o3, l3 = fn(qf[-3:], k, v, 0.5, True)
+    o1, l1 = fn(qf[-1:], k, v, 0.5, True)
+    on, ln_ = fn(qf[-1:], k, v, 0.5, False)
+    return (np.allclose(o3, of[-3:], atol=1e-14) and np.allclose(l3, lf[-3:], atol=1e-14)
+            and np.allclose(o1, on, atol=1e-15) and np.allclose(l1, ln_, atol=1e-15))
+
+
+PIN_CHECKS = {
+    "tkv1": _pin_tkv1,
+    "zero_query": _pin_zero_query,
+    "ones_value": _pin_ones_value,
+    "causal_row0": _pin_causal_row0,
+    "two_keys": _pin_two_keys,
+    "key_shift": _pin_key_shift,
+    "permutation": _pin_permutation,
+    "brute_force": _pin_brute,
+    "torch_sdpa": _pin_torch_sdpa,
+    "causal_suffix": _pin_causal_suffix,
+}
+
+
+def _oracle_2d(q, k, v, scale, causal):
+    return attention(q, k, v, scale, causal)
+
+
+@pytest.mark.parametrize("name", sorted(PIN_CHECKS))
+def test_oracle_pin(name):
+    assert PIN_CHECKS[name](_oracle_2d)
+
+
+# Plausible mistakes, planted in copies of the oracle (CPU only).  Each must
+# be rejected by at least one pin.
+
+def _mut_no_scale(q, k, v, scale, causal):
+    return attention(q, k, v, 1.0, causal)
+
+
+def _mut_wrong_axis(q, k, v, scale, causal):
+    s = (q @ k.T) * scale
+    if causal:
+        tq, tkv = s.shape
+        s[np.arange(tkv)[None, :] > np.arange(tq)[:, None] + tkv - tq] = -np.inf
+    m = s.max(axis=0, keepdims=True)
+    p = np.exp(s - m)
+    l = p.sum(axis=0, keepdims=True)
+    p = p / l
+    return p @ v, (m + np.log(l)).ravel()[: s.shape[0]] if s.shape[1] >= s.shape[0] else np.zeros(s.shape[0])
+
+
+def _mut_flipped_mask(q, k, v, scale, causal):
+    if not causal:
+        return attention(q, k, v, scale, False)
+    s = (q @ k.T) * scale
+    tq, tkv = s.shape
+    s[np.arange(tkv)[None, :] < np.arange(tq)[:, None] + tkv - tq] = -np.inf
+    m = s.max(axis=1)
+    p = np.exp(s - m[:, None])
+    l = p.sum(axis=1)
+    return (p @ v) / l[:, None], m + np.log(l)
+
+
+def _mut_strict_diagonal(q, k, v, scale, causal):
+    if not causal:
+        return attention(q, k, v, scale, False)
+    s = (q @ k.T) * scale
+    tq, tkv = s.shape
+    s[np.arange(tkv)[None, :] >= np.arange(tq)[:, None] + tkv - tq] = -np.inf
+    s[0, 0] = 0.0 if tq == tkv else s[0, 0]
+    m = s.max(axis=1)
+    p = np.exp(s - m[:, None])
+    l = p.sum(axis=1)
+    return (p @ v) / l[:, None], m + np.log(l)
+
+
+def _mut_top_left_causal(q, k, v, scale, causal):
+    if not causal:
+        return attention(q, k, v, scale, False)
+    s = (q @ k.T) * scale
+    tq, tkv = s.shape
+    s[np.arange(tkv)[None, :] > np.arange(tq)[:, None]] = -np.inf
+    m = s.max(axis=1)
+    p = np.exp(s - m[:, None])
+    l = p.sum(axis=1)
+    return (p @ v) / l[:, None], m + np.log(l)
+
+
+def _mut_lse_drops_max(q, k, v, scale, causal):
+    o, lse = attention(q, k, v, scale, causal)
+    s = (q @ k.T) * scale
+    if causal:
+        tq, tkv = s.shape
+        s[np.arange(tkv)[None, :] > np.arange(tq)[:, None] + tkv - tq] = -np.inf
+    return o, lse - s.max(axis=1)
+
+
+def _mut_log2_lse(q, k, v, scale, causal):
+    o, lse = attention(q, k, v, scale, causal)
+    return o, lse / math.log(2.0)
+
+
+def _mut_no_normalise(q, k, v, scale, causal):
+    s = (q @ k.T) * scale
+    if causal:
+        tq, tkv = s.shape
+        s[np.arange(tkv)[None, :] > np.arange(tq)[:, None] + tkv - tq] = -np.inf
+    m = s.max(axis=1)
+    p = np.exp(s - m[:, None])
+    return p @ v, m + np.log(p.sum(axis=1))
+
+
+def _mut_transposed_value(q, k, v, scale, causal):
+    o, lse = attention(q, k, v, scale, causal)
+    vv = v[::-1].copy()
+    o2, _ = attention(q, k, vv, scale, causal)
+    return o2, lse
+
+
+def _mut_key_query_swapped(q, k, v, scale, causal):
+    # uses k as queries against q as keys when shapes allow it
+    if q.shape == k.shape:
+        s = (k @ q.T) * scale
+    else:
+        s = (q @ k.T) * scale
+    if causal:
+        tq, tkv = s.shape
+        s[np.arange(tkv)[None, :] > np.arange(tq)[:, None] + tkv - tq] = -np.inf
+    m = s.max(axis=1)
+    p = np.exp(s - m[:, None])
+    l = p.sum(axis=1)
+    return (p @ v) / l[:, None], m + np.log(l)
+
+
+MUTANTS = {
+    "no_scale": _mut_no_scale,
+    "wrong_axis": _mut_wrong_axis,
+    "flipped_mask": _mut_flipped_mask,
+    "strict_diagonal": _mut_strict_diagonal,
+    "top_left_causal": _mut_top_left_causal,
+    "lse_drops_max": _mut_lse_drops_max,
+    "log2_lse": _mut_log2_lse,
+    "no_normalise": _mut_no_normalise,
+    "reversed_value_rows": _mut_transposed_value,
+    "key_query_swapped": _mut_key_query_swapped,
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_reject_planted_mistake(name):
+    fn = MUTANTS[name]
+    failed = []
+    for pin, check in PIN_CHECKS.items():
+        try:
+            ok = check(fn)
+        except Exception:
+            ok = False
+        if not ok:
+            failed.append(pin)
+    assert failed, f"mutant {name} passed every pin"
+
+
+# ---------------------------------------------------------------- API behaviour
+
+def test_rows_argument_matches_full_rows():
+    rng = np.random.default_rng(21)
+    q, k, v = _rand(rng, 2, 3, 12, 4), _rand(rng, 2, 3, 12, 4), _rand(rng, 2, 3, 12, 5)
+    rows = np.array([0, 5, 11, 3])
+    for causal in (False, True):
+        o, lse = attention(q, k, v, 0.5, causal)
+        o_r, lse_r = attention(q, k, v, 0.5, causal, rows=rows)
+        np.testing.assert_array_equal(o_r, o[..., rows, :])
+        np.testing.assert_array_equal(lse_r, lse[..., rows])
+
+
+def test_leading_axes_are_independent():
+    rng = np.random.default_rng(22)
+    q, k, v = _rand(rng, 2, 3, 6, 4), _rand(rng, 2, 3, 8, 4), _rand(rng, 2, 3, 8, 5)
+    o, lse = attention(q, k, v, 0.5, True)
+    for b in range(2):
+        for h in range(3):
+            ob, lb = attention(q[b, h], k[b, h], v[b, h], 0.5, True)
+            np.testing.assert_array_equal(o[b, h], ob)
+            np.testing.assert_array_equal(lse[b, h], lb)
+
+
+def test_causal_query_longer_than_keys_rejected():
+    rng = np.random.default_rng(23)
+    with pytest.raises(ValueError):
+        attention(_rand(rng, 5, 4), _rand(rng, 4, 4), _rand(rng, 4, 2), 0.5, causal=True)
+
+
+def test_large_scores_are_stable():
+    rng = np.random.default_rng(24)
+    q, k, v = 40.0 * _rand(rng, 4, 8), 40.0 * _rand(rng, 16, 8), _rand(rng, 16, 3)
+    o, lse = attention(q, k, v, 1.0, False)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    ob, lb = _brute(q, k, v, 1.0, False)
+    np.testing.assert_allclose(o, ob, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(lse, lb, rtol=1e-13)
+
+
+@pytest.mark.parametrize("num_splits", [1, 2, 3, 16, 40, 43])
+def test_split_combine_equals_unsplit(num_splits):
+    rng = np.random.default_rng(25)
+    q, k, v = _rand(rng, 2, 3, 1, 8), 3 * _rand(rng, 2, 3, 40, 8), _rand(rng, 2, 3, 40, 6)
+    o, lse = attention(q, k, v, 0.35)
+    o_s, lse_s = oracle.split_attention(q, k, v, 0.35, num_splits)
+    np.testing.assert_allclose(o_s, o, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse_s, lse, rtol=1e-13, atol=1e-13)
+
+
+def test_split_below_one_raises():
+    rng = np.random.default_rng(26)
+    with pytest.raises(ValueError):
+        oracle.split_attention(_rand(rng, 1, 4), _rand(rng, 4, 4), _rand(rng, 4, 2), 0.5, 0)
