@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gpt2]
+
+Prints ONE JSON line on stdout (progress goes to stderr).  A step is one call
+of the attention forward over one batch of the workload (default: GPT-2-shaped
+causal prefill, B=4, H=12, T=1024, d=64, bf16): the prefill kernel runs every
+prefill step of the hot path (Q tile load, K/V streaming, both products, the
+online softmax, causal skipping, the epilogue).  The decode half of the path
+(split-KV kernel + combine) is timed the same way on its own workload
+(B=64, H=32, T_kv=8192, d=128, 16 partitions) and reported in "decode".
+
+Inputs are seeded synthetic tensors already resident in HBM when timing
+starts; W untimed warm-up steps are followed by exactly K timed steps,
+bracketed by device synchronisation, with HIP events recorded on the stream
+the kernels are launched on.  The float64 oracle is timed on the host cores on
+a bounded sample (the "cpu_baseline" leg) and checks the GPU output.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def visible_pairs(tq: int, tkv: int, causal: bool) -> int:
+    """(query, key) pairs attention touches; causal uses bottom-right alignment."""
+    if not causal:
+        return tq * tkv
+    off = tkv - tq
+    return tq * (off + 1) + tq * (tq - 1) // 2
+
+
+def prefill_flops(w) -> int:
+    return 4 * w.B * w.H * w.d * visible_pairs(w.Tq, w.Tkv, w.causal)
+
+
+def prefill_bytes(w) -> int:
+    es = 2 if w.dtype == "bf16" else 4
+    return w.B * w.H * ((2 * w.Tq + 2 * w.Tkv) * w.d * es + w.Tq * 4)
+
+
+def decode_bytes(w) -> tuple[int, int]:
+    kv = 2 * w.B * w.H * w.Tkv * w.d * 2
+    return kv + 2 * w.B * w.H * w.d * 2 + w.B * w.H * 4, kv
+
+
+def kernel_sources_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "io_aware_exact_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_prefix: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, only if
+    they were taken on the current kernel sources; otherwise None."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        e = rec.get(workload, {}).get(kernel_prefix)
+        if not e or e.get("sources_sha256_16") != kernel_sources_digest():
+            return None
+        return int(e["fetch_bytes"] + e["write_bytes"])
+    except (OSError, ValueError, KeyError, TypeError):
+        return None
+
+
+def time_steps(torch, call, steps: int, warmup: int):
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        call()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def cpu_baseline_prefill(w, q, k, v, o_gpu, lse_gpu, min_seconds: float):
+    """Oracle leg: the float64 oracle on the host, over whole (b, h) heads of
+    the same inputs until about ``min_seconds`` of CPU work is done; also the
+    parity of the GPU output on those heads."""
+    import numpy as np
+
+    import oracle
+    from io_aware_exact_amd.inputs import to_f64
+
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done, t_compute, err_o, err_l = 0, 0.0, 0.0, 0.0
+    t_wall0 = time.perf_counter()
+    while t_compute < min_seconds:
+        b, h = heads[done % len(heads)]
+        qb, kb, vb = to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h])
+        t0 = time.perf_counter()
+        o_ref, lse_ref = oracle.attention(qb, kb, vb, w.scale, w.causal)
+        t_compute += time.perf_counter() - t0
+        if done < len(heads):
+            err_o = max(err_o, float(np.abs(to_f64(o_gpu[b, h]) - o_ref).max()))
+            err_l = max(err_l, float(np.abs(to_f64(lse_gpu[b, h]) - lse_ref).max()))
+        done += 1
+    passes = done / len(heads)
+    per_head = 4 * w.d * visible_pairs(w.Tq, w.Tkv, w.causal)
+    value = per_head * done / t_compute / 1e12
+    return {
+        "value": value,
+        "unit": "TFLOP/s",
+        "cores": blas_threads(),
+        "host_cpus": os.cpu_count(),
+        "kind": "oracle",
+        "sample": f"{done} (batch, head) slices of this workload ({passes:.2f} x its {len(heads)} slices), "
+                  f"float64 numpy, full T_q x T_kv scores materialised per head; causal-adjusted flop count",
+        "seconds": t_compute,
+        "wall_seconds": time.perf_counter() - t_wall0,
+    }, {"max_abs_err_o": err_o, "max_abs_err_lse": err_l, "heads_checked": min(done, len(heads))}
+
+
+def run_decode(torch, attn, steps, warmup):
+    import numpy as np
+
+    import oracle
+    from io_aware_exact_amd.inputs import WORKLOADS, make_qkv, to_f64
+
+    w = WORKLOADS["decode"]
+    log(f"[bench] decode workload {w}: generating inputs")
+    t0 = time.perf_counter()
+    q, k, v = make_qkv(w)
+    dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
+    log(f"[bench] decode inputs ready in {time.perf_counter() - t0:.1f}s")
+    o = torch.empty_like(dq)
+    lse = torch.empty((w.B, w.H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(attn.attn_decode_workspace_bytes(w.B, w.H, w.d, w.num_splits), dtype=torch.uint8, device="cuda")
+    call = attn.prepared_decode(dq, dk, dv, o, lse, w.num_splits, ws, w.scale)
+    ms = time_steps(torch, call, steps, warmup)
+    kern = attn.attn_last_kernel()
+    total, kv = decode_bytes(w)
+    gbps = total / (ms * 1e-3) / 1e9
+    # parity on sampled heads (oracle = the definition per head)
+    rng = np.random.default_rng(5)
+    errs_o, errs_l = [], []
+    for b, h in [(0, 0), (w.B - 1, w.H - 1)] + list(zip(rng.integers(0, w.B, 6).tolist(), rng.integers(0, w.H, 6).tolist())):
+        o_ref, lse_ref = oracle.attention(to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]), w.scale)
+        errs_o.append(float(np.abs(to_f64(o[b, h]) - o_ref).max()))
+        errs_l.append(float(abs(float(lse[b, h]) - lse_ref[0])))
+    # oracle leg, bounded: a few heads on the host
+    sample_heads = 32
+    t0 = time.perf_counter()
+    for i in range(sample_heads):
+        b, h = i % w.B, (7 * i) % w.H
+        oracle.attention(to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]), w.scale)
+    t_cpu = time.perf_counter() - t0
+    cpu_gbps = sample_heads * (total / (w.B * w.H)) / t_cpu / 1e9
+    del dq, dk, dv, q, k, v
+    torch.cuda.empty_cache()
+    return {
+        "workload": f"decode B={w.B} H={w.H} Tq=1 Tkv={w.Tkv} d={w.d} bf16 splits={w.num_splits}",
+        "metric": "decode attention KV-cache read bandwidth",
+        "value": gbps,
+        "unit": "GB/s",
+        "kv_only_GBps": kv / (ms * 1e-3) / 1e9,
+        "ms_per_step": ms,
+        "steps": steps,
+        "warmup": warmup,
+        "kernel": kern,
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": gbps / PEAK_HBM_GBPS, "traffic": measured_traffic("decode", "decode")},
+        "parity": {"max_abs_err_o": max(errs_o), "max_abs_err_lse": max(errs_l), "heads_checked": len(errs_o)},
+        "cpu_baseline": {"value": cpu_gbps, "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
+                         "sample": f"{sample_heads} (batch, head) slices, float64 numpy definition"},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gpt2", help="prefill workload: gpt2, mid, mid_causal, long, tiny")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle leg: seconds of CPU work")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the attention forward has no multi-GPU path in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import io_aware_exact_amd as attn
+    from io_aware_exact_amd.inputs import WORKLOADS, make_qkv
+
+    if not os.path.exists(attn.attn.LIB_PATH):
+        from io_aware_exact_amd import build as _build
+        _build.build()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    w = WORKLOADS[args.workload]
+    log(f"[bench] prefill workload {w}")
+    q, k, v = make_qkv(w)
+    dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
+    o = torch.empty_like(dq)
+    lse = torch.empty((w.B, w.H, w.Tq), dtype=torch.float32, device="cuda")
+    call = attn.prepared_fwd(dq, dk, dv, o, lse, w.causal, w.scale, f32=(w.dtype == "f32"))
+    ms = time_steps(torch, call, args.steps, args.warmup)
+    kern = attn.attn_last_kernel()
+    flops = prefill_flops(w)
+    nbytes = prefill_bytes(w)
+    tflops = flops / (ms * 1e-3) / 1e12
+    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBPS * 1e9)
+    if t_hbm > t_mfma:
+        ach = nbytes / (ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBPS}
+    else:
+        roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": tflops / PEAK_BF16_TFLOPS}
+    roof["traffic"] = measured_traffic("prefill", w.name)
+    log(f"[bench] prefill {kern}: {ms * 1e3:.2f} us/step, {tflops:.1f} TFLOP/s")
+
+    result = {
+        "metric": "attn fwd TFLOP/s (causal-adjusted) & % bf16 MFMA peak (prefill); decode KV GB/s & % HBM peak",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} prefill B={w.B} H={w.H} Tq={w.Tq} Tkv={w.Tkv} d={w.d} "
+                               f"{'causal' if w.causal else 'non-causal'} {w.dtype}",
+                   "B": w.B, "H": w.H, "Tq": w.Tq, "Tkv": w.Tkv, "d": w.d, "causal": w.causal,
+                   "scale": w.scale, "parallelism": "none (1 GPU)"},
+        "kernel": kern,
+        "pct_of_peak": {"bf16_mfma": 100.0 * tflops / PEAK_BF16_TFLOPS,
+                        "hbm_algorithmic": 100.0 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS},
+        "roofline": roof,
+        "extra_device_bytes": 0,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] oracle leg on the host")
+        torch.cuda.synchronize()
+        cpu, parity = cpu_baseline_prefill(w, q, k, v, o.cpu(), lse.cpu(), args.cpu_seconds)
+        result["cpu_baseline"] = cpu
+        result["parity"] = parity
+        log(f"[bench] oracle {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads; parity {parity}")
+    else:
+        result["cpu_baseline"] = None
+    del dq, dk, dv
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        result["decode"] = run_decode(torch, attn, args.steps, args.warmup)
+        log(f"[bench] decode {result['decode']['kernel']}: {result['decode']['ms_per_step']:.3f} ms/step, "
+            f"{result['decode']['value']:.0f} GB/s")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,133 @@
+/*
+ * Exact IO-aware attention forward for AMD MI355X (gfx950) -- C ABI.
+ *
+ * Every entry point computes, for each (batch b, head h),
+ *
+ *     S = scale * Q K^T          (T_q x T_kv; never written to memory)
+ *     S[i, j] = -inf  where causal and j > i + (T_kv - T_q)
+ *     O = softmax_rows(S) V,     LSE_i = ln sum_j exp(S[i, j])
+ *
+ * i.e. the definition of "FlashAttention IO-aware tiling lab" (S = QK^T /
+ * sqrt(d), P = softmax(S), O = PV) and of "Attention and Its Computational
+ * Cost", section "What is being computed", evaluated block by block with the
+ * running-max / running-sum recurrence of "IO-Aware Attention: Tiling the
+ * Score Matrix Without Materializing It", section "Softmax over blocks,
+ * exactly".  The causal rule is aligned to the bottom-right corner, so for
+ * self-attention (T_q == T_kv) row i sees keys 0..i, and a single new query
+ * sees every cached key.  LSE is the natural-log normaliser of each row in
+ * units of the scaled score, kept for a backward pass ("IO-Aware Attention",
+ * section "What has to stay in fast memory").
+ *
+ * Layout: Q and O are [B, H, T_q, d], K and V are [B, H, T_kv, d], all
+ * contiguous row-major with d innermost; LSE is [B, H, T_q] fp32.  bf16 data
+ * is passed as 16-bit words (the upper half of the IEEE fp32 bit pattern).
+ *
+ * Ownership: every pointer is caller-owned device memory.  The library never
+ * allocates, frees or retains a pointer past the call.  Inputs must not alias
+ * outputs or the workspace.
+ *
+ * Execution: calls are asynchronous on `stream` (NULL = the null stream) and
+ * return once the kernels are enqueued; results are valid after the stream is
+ * synchronised.  There is no internal synchronisation and no host<->device
+ * copy.
+ *
+ * Errors: arguments are validated before any HIP call; a failing call
+ * enqueues nothing and returns one of the negative codes below, with a
+ * thread-local description in attn_status_string().  No call aborts.
+ */
+#ifndef IO_AWARE_EXACT_ATTN_H
+#define IO_AWARE_EXACT_ATTN_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    ATTN_OK = 0,
+    ATTN_EINVAL = -1,       /* null pointer, size < 1, scale not finite or <= 0, causal with T_q > T_kv,
+                               pointer not 16-byte aligned, num_splits < 1, aliasing output, sizes overflow */
+    ATTN_EUNSUPPORTED = -2, /* head width d not built for this path */
+    ATTN_EHIP = -3,         /* the HIP runtime reported an error while enqueueing */
+    ATTN_EWORKSPACE = -4    /* decode workspace missing or smaller than attn_decode_workspace_bytes() */
+};
+
+/*
+ * attn_fwd -- bf16 attention forward (prefill, or decode when T_q == 1).
+ *
+ *   q, k, v  device pointers to bf16 Q [B,H,Tq,d], K and V [B,H,Tkv,d]
+ *   o        device pointer to bf16 O [B,H,Tq,d] (written)
+ *   lse      device pointer to fp32 LSE [B,H,Tq] (written), or NULL to skip it
+ *   causal   0 or 1 (bottom-right aligned mask; needs Tq <= Tkv)
+ *   scale    multiplier of q.k, finite and > 0 (the pages use 1/sqrt(d))
+ *
+ * Products use bf16 MFMA with fp32 accumulation; the softmax statistics and
+ * the output accumulator are fp32 ("IO-Aware Attention", section "Where the
+ * approach stops helping": 32-bit accumulation and rescaling); P is rounded to
+ * bf16 (nearest even) before the PV product and O is rounded once at the end.
+ * Supported: d = 64 for T_q > 1; d in {64, 128} for T_q == 1 (runs the decode
+ * kernel unsplit, no workspace).  T_q and T_kv need not be multiples of any tile.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int Tq, int Tkv, int d, int causal, float scale, hipStream_t stream);
+
+/*
+ * attn_fwd_f32 -- the exact path: fp32 inputs, fp32 products, fp32 output.
+ * Same arguments and semantics as attn_fwd with every tensor fp32.
+ * Supported: d in {16, 32, 64, 128}, any T_q >= 1, T_kv >= 1.
+ */
+int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                 int B, int H, int Tq, int Tkv, int d, int causal, float scale, hipStream_t stream);
+
+/*
+ * attn_decode_workspace_bytes -- bytes of workspace attn_decode needs:
+ * B*H*num_splits*(d+2)*4 (one fp32 partial output of d values plus its
+ * running max and running sum per partition), 0 when num_splits <= 1 or any
+ * size is < 1.
+ */
+size_t attn_decode_workspace_bytes(int B, int H, int d, int num_splits);
+
+/*
+ * attn_decode -- one query per (batch, head) against T_kv cached keys, with
+ * the key axis split into num_splits partitions ("IO-Aware Attention",
+ * section "Parallelism and the cost of the split": each partition produces a
+ * partial output and normaliser, merged with the same rescaling in a second
+ * kernel on the same stream).
+ *
+ *   q, o       bf16 [B,H,1,d];  k, v bf16 [B,H,Tkv,d];  lse fp32 [B,H] or NULL
+ *   scale      finite and > 0
+ *   num_splits >= 1; values above Tkv are clamped to Tkv.  Partition p covers
+ *              keys [floor(p*Tkv/P), floor((p+1)*Tkv/P)).
+ *   workspace  device memory of at least attn_decode_workspace_bytes(B,H,d,num_splits)
+ *              bytes (may be NULL when num_splits == 1); contents on entry are ignored.
+ *
+ * Supported: d in {64, 128}.
+ */
+int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                int B, int H, int Tkv, int d, float scale, int num_splits,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * attn_last_kernel -- name and tile configuration of the kernel(s) enqueued by
+ * this thread's last successful call, e.g.
+ * "prefill_bf16_d64<waves=4,bq=128,bk=64,causal>" ("Attention and Its
+ * Computational Cost", section "Which kernel ran": a measurement of attention
+ * names the kernel that ran).  Empty before the first call.  The string is
+ * thread-local and valid until this thread's next call.
+ */
+const char* attn_last_kernel(void);
+
+/*
+ * attn_status_string -- description of `status`; for the calling thread's most
+ * recent failure with that code it carries the detail (which argument, or the
+ * HIP error text).  Thread-local storage, valid until the next call.
+ */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IO_AWARE_EXACT_ATTN_H */

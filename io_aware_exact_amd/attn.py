@@ -1,0 +1,202 @@
+"""Python binding of the C ABI in include/attn.h (ctypes; marshalling only).
+
+Every step of the computation runs in the HIP kernels of ``libattn.so``.
+PyTorch provides device memory and the current stream.  There is no fallback:
+if the library is missing or a tensor is not on a GPU, the call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+ATTN_OK = 0
+ATTN_EINVAL = -1
+ATTN_EUNSUPPORTED = -2
+ATTN_EHIP = -3
+ATTN_EWORKSPACE = -4
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+
+# name -> (restype, argtypes), in the order of include/attn.h
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_S = ctypes.c_size_t
+SIGNATURES = {
+    "attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "attn_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "attn_decode_workspace_bytes": (_S, [_I, _I, _I, _I]),
+    "attn_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _S, _P]),
+    "attn_last_kernel": (ctypes.c_char_p, []),
+    "attn_status_string": (ctypes.c_char_p, [_I]),
+}
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"attn status {status}: {detail}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libattn.so (built in-tree) and declare its signatures."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build the HIP extension first "
+                "(python -m io_aware_exact_amd.build, or __graft_entry__.build())")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status == ATTN_OK:
+        return
+    detail = lib().attn_status_string(status).decode()
+    if status in (ATTN_EINVAL, ATTN_EWORKSPACE):
+        raise ValueError(f"attn status {status}: {detail}")
+    if status == ATTN_EUNSUPPORTED:
+        raise NotImplementedError(f"attn status {status}: {detail}")
+    raise AttnError(status, detail)
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (the attention path has no CPU fallback)")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _shape4(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, T, d]")
+    B, H, Tq, d = q.shape
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    return B, H, Tq, k.shape[2], d
+
+
+def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
+             return_lse: bool = True):
+    """bf16 attention forward; q [B,H,Tq,d], k/v [B,H,Tkv,d] -> (o, lse)."""
+    B, H, Tq, Tkv, d = _shape4(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, Tq), dtype=torch.float32, device=q.device)
+    lp = _dev(lse, "lse", torch.float32) if return_lse else None
+    st = lib().attn_fwd(_dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16), _dev(v, "v", torch.bfloat16),
+                        _dev(o, "o", torch.bfloat16), lp, B, H, Tq, Tkv, d, int(bool(causal)), scale, _stream())
+    _check(st)
+    return (o, lse) if return_lse else o
+
+
+def attn_fwd_f32(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
+                 return_lse: bool = True):
+    """fp32 attention forward (exact path); same contract as attn_fwd."""
+    B, H, Tq, Tkv, d = _shape4(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, Tq), dtype=torch.float32, device=q.device)
+    lp = _dev(lse, "lse", torch.float32) if return_lse else None
+    st = lib().attn_fwd_f32(_dev(q, "q", torch.float32), _dev(k, "k", torch.float32), _dev(v, "v", torch.float32),
+                            _dev(o, "o", torch.float32), lp, B, H, Tq, Tkv, d, int(bool(causal)), scale, _stream())
+    _check(st)
+    return (o, lse) if return_lse else o
+
+
+def attn_decode_workspace_bytes(B: int, H: int, d: int, num_splits: int) -> int:
+    return int(lib().attn_decode_workspace_bytes(B, H, d, num_splits))
+
+
+def attn_decode(q, k, v, scale: float | None = None, num_splits: int = 16, workspace=None, out=None, lse=None,
+                return_lse: bool = True):
+    """One query per (batch, head): q [B,H,1,d], k/v [B,H,Tkv,d] -> (o, lse [B,H]).
+
+    ``workspace`` (a uint8 GPU tensor) is allocated when not given.
+    """
+    B, H, Tq, Tkv, d = _shape4(q, k, v)
+    if Tq != 1:
+        raise ValueError("attn_decode takes exactly one query per (batch, head)")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    lp = _dev(lse, "lse", torch.float32) if return_lse else None
+    splits = max(1, min(int(num_splits), Tkv))
+    need = attn_decode_workspace_bytes(B, H, d, splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wp, wbytes = (None, 0) if workspace is None else (_dev(workspace, "workspace", workspace.dtype),
+                                                      workspace.numel() * workspace.element_size())
+    st = lib().attn_decode(_dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16), _dev(v, "v", torch.bfloat16),
+                           _dev(o, "o", torch.bfloat16), lp, B, H, Tkv, d, scale, int(num_splits), wp, wbytes,
+                           _stream())
+    _check(st)
+    return (o, lse) if return_lse else o
+
+
+def attn_last_kernel() -> str:
+    return lib().attn_last_kernel().decode()
+
+
+def attn_status_string(status: int) -> str:
+    return lib().attn_status_string(int(status)).decode()
+
+
+def prepared_fwd(q, k, v, o, lse, causal: bool, scale: float | None = None, f32: bool = False):
+    """A zero-argument callable that enqueues attn_fwd (or attn_fwd_f32) on
+    the current stream with these tensors; argument checks happen once here,
+    so repeated launches (benchmark loops) cost only the C call."""
+    B, H, Tq, Tkv, d = _shape4(q, k, v)
+    dt = torch.float32 if f32 else torch.bfloat16
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    ptrs = [_dev(t, n, dt) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"))]
+    lp = None if lse is None else _dev(lse, "lse", torch.float32)
+    fn = lib().attn_fwd_f32 if f32 else lib().attn_fwd
+    stream = _stream()
+    args = (*ptrs, lp, B, H, Tq, Tkv, d, int(bool(causal)), scale, stream)
+
+    def call():
+        _check(fn(*args))
+
+    return call
+
+
+def prepared_decode(q, k, v, o, lse, num_splits: int, workspace, scale: float | None = None):
+    """Zero-argument callable enqueuing attn_decode; see prepared_fwd."""
+    B, H, Tq, Tkv, d = _shape4(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    ptrs = [_dev(t, n, torch.bfloat16) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"))]
+    lp = None if lse is None else _dev(lse, "lse", torch.float32)
+    wp, wb = (None, 0) if workspace is None else (_dev(workspace, "workspace", workspace.dtype),
+                                                  workspace.numel() * workspace.element_size())
+    fn = lib().attn_decode
+    args = (*ptrs, lp, B, H, Tkv, d, scale, int(num_splits), wp, wb, _stream())
+
+    def call():
+        _check(fn(*args))
+
+    return call

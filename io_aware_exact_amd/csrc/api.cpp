@@ -1,0 +1,177 @@
+// C ABI of the attention library: argument validation, shape-based kernel
+// choice and error reporting.  Validation happens before any HIP call, so a
+// rejected call touches neither the device nor the runtime.
+#include "attn.h"
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_detail;
+thread_local int g_detail_code = 0;
+thread_local std::string g_last_kernel;
+
+constexpr double kLog2e = 1.4426950408889634074;
+
+int fail(int code, const std::string& what) {
+    g_detail_code = code;
+    g_detail = what;
+    return code;
+}
+
+const char* generic(int status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_EINVAL: return "invalid argument";
+        case ATTN_EUNSUPPORTED: return "unsupported configuration";
+        case ATTN_EHIP: return "HIP runtime error";
+        case ATTN_EWORKSPACE: return "workspace missing or too small";
+        default: return "unknown status";
+    }
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;
+    const char* name;
+};
+
+bool overlap(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Checks shared by every entry point.  `es` is the element size of q/k/v/o.
+int check_common(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H,
+                 int Tq, int Tkv, int d, int causal, float scale, size_t es) {
+    if (!q) return fail(ATTN_EINVAL, "q is NULL");
+    if (!k) return fail(ATTN_EINVAL, "k is NULL");
+    if (!v) return fail(ATTN_EINVAL, "v is NULL");
+    if (!o) return fail(ATTN_EINVAL, "o is NULL");
+    if (B < 1) return fail(ATTN_EINVAL, "B must be >= 1");
+    if (H < 1) return fail(ATTN_EINVAL, "H must be >= 1");
+    if (Tq < 1) return fail(ATTN_EINVAL, "Tq must be >= 1");
+    if (Tkv < 1) return fail(ATTN_EINVAL, "Tkv must be >= 1");
+    if (d < 1) return fail(ATTN_EINVAL, "d must be >= 1");
+    if (causal != 0 && causal != 1) return fail(ATTN_EINVAL, "causal must be 0 or 1");
+    if (!std::isfinite(scale) || !(scale > 0.f)) return fail(ATTN_EINVAL, "scale must be finite and > 0");
+    if (causal && Tq > Tkv) return fail(ATTN_EINVAL, "causal attention needs Tq <= Tkv");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+        return fail(ATTN_EINVAL, "q, k, v and o must be 16-byte aligned");
+    if (lse && !aligned(lse, 4)) return fail(ATTN_EINVAL, "lse must be 4-byte aligned");
+    // sizes: B*H*T*d*es must fit comfortably in 63 bits
+    const double qbytes = double(B) * H * Tq * d * es;
+    const double kbytes = double(B) * H * Tkv * d * es;
+    if (qbytes > 4.0e18 || kbytes > 4.0e18) return fail(ATTN_EINVAL, "tensor sizes overflow");
+    const uint64_t BH = uint64_t(B) * uint64_t(H);
+    if (BH > 0x7fffffffull) return fail(ATTN_EINVAL, "B*H must fit in 31 bits");
+    const Range rq{reinterpret_cast<uintptr_t>(q), reinterpret_cast<uintptr_t>(q) + uint64_t(qbytes), "q"};
+    const Range rk{reinterpret_cast<uintptr_t>(k), reinterpret_cast<uintptr_t>(k) + uint64_t(kbytes), "k"};
+    const Range rv{reinterpret_cast<uintptr_t>(v), reinterpret_cast<uintptr_t>(v) + uint64_t(kbytes), "v"};
+    const Range ro{reinterpret_cast<uintptr_t>(o), reinterpret_cast<uintptr_t>(o) + uint64_t(qbytes), "o"};
+    for (const Range* in : {&rq, &rk, &rv})
+        if (overlap(ro, *in)) return fail(ATTN_EINVAL, std::string("o overlaps ") + in->name);
+    if (lse) {
+        const Range rl{reinterpret_cast<uintptr_t>(lse), reinterpret_cast<uintptr_t>(lse) + BH * uint64_t(Tq) * 4,
+                       "lse"};
+        for (const Range* other : {&rq, &rk, &rv, &ro})
+            if (overlap(rl, *other)) return fail(ATTN_EINVAL, std::string("lse overlaps ") + other->name);
+    }
+    return ATTN_OK;
+}
+
+int finish(hipError_t e, const char* name) {
+    if (e != hipSuccess) return fail(ATTN_EHIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+    g_last_kernel = name ? name : "";
+    return ATTN_OK;
+}
+
+int run_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Tkv, int d,
+               float scale, int splits, void* ws, hipStream_t stream) {
+    attn::DecodeArgs a{q, k, v, o, lse, B, H, Tkv, d, splits, float(double(scale) * kLog2e), ws};
+    const char* name = nullptr;
+    (void)hipGetLastError();   // clear any stale error so the launch status is ours
+    return finish(attn::launch_decode_bf16(a, stream, &name), name);
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Tq, int Tkv,
+             int d, int causal, float scale, hipStream_t stream) {
+    int st = check_common(q, k, v, o, lse, B, H, Tq, Tkv, d, causal, scale, 2);
+    if (st != ATTN_OK) return st;
+    if (Tq == 1) {
+        // a single query row: the decode kernel, unsplit (bottom-right causal
+        // alignment lets the one row see every key, so causal changes nothing)
+        if (d != 64 && d != 128) return fail(ATTN_EUNSUPPORTED, "bf16 single-query path supports d in {64, 128}");
+        return run_decode(q, k, v, o, lse, B, H, Tkv, d, scale, 1, nullptr, stream);
+    }
+    if (d != 64) return fail(ATTN_EUNSUPPORTED, "bf16 prefill supports d = 64");
+    if (double(B) * H * ((Tq + 127) / 128) > 2147483647.0) return fail(ATTN_EINVAL, "grid too large");
+    attn::PrefillArgs a{q, k, v, o, lse, B, H, Tq, Tkv, d, causal != 0, float(double(scale) * kLog2e)};
+    const char* name = nullptr;
+    (void)hipGetLastError();
+    return finish(attn::launch_prefill_bf16_d64(a, stream, &name), name);
+}
+
+int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int Tq,
+                 int Tkv, int d, int causal, float scale, hipStream_t stream) {
+    int st = check_common(q, k, v, o, lse, B, H, Tq, Tkv, d, causal, scale, 4);
+    if (st != ATTN_OK) return st;
+    if (!attn::prefill_f32_supports(d)) return fail(ATTN_EUNSUPPORTED, "fp32 path supports d in {16, 32, 64, 128}");
+    if (double(B) * H * Tq > 2147483647.0) return fail(ATTN_EINVAL, "grid too large");
+    attn::PrefillArgs a{q, k, v, o, lse, B, H, Tq, Tkv, d, causal != 0, float(double(scale) * kLog2e)};
+    const char* name = nullptr;
+    (void)hipGetLastError();
+    return finish(attn::launch_prefill_f32(a, stream, &name), name);
+}
+
+size_t attn_decode_workspace_bytes(int B, int H, int d, int num_splits) {
+    if (B < 1 || H < 1 || d < 1 || num_splits <= 1) return 0;
+    return size_t(B) * size_t(H) * size_t(num_splits) * size_t(d + 2) * sizeof(float);
+}
+
+int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Tkv, int d,
+                float scale, int num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    int st = check_common(q, k, v, o, lse, B, H, 1, Tkv, d, 0, scale, 2);
+    if (st != ATTN_OK) return st;
+    if (num_splits < 1) return fail(ATTN_EINVAL, "num_splits must be >= 1");
+    if (d != 64 && d != 128) return fail(ATTN_EUNSUPPORTED, "decode supports d in {64, 128}");
+    const int splits = num_splits > Tkv ? Tkv : num_splits;
+    if (splits > 65535) return fail(ATTN_EUNSUPPORTED, "decode supports at most 65535 partitions");
+    if (splits > 1) {
+        const size_t need = attn_decode_workspace_bytes(B, H, d, splits);
+        if (!workspace) return fail(ATTN_EWORKSPACE, "workspace is NULL");
+        if (workspace_bytes < need)
+            return fail(ATTN_EWORKSPACE, "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " +
+                                             std::to_string(need));
+        if (!aligned(workspace, 16)) return fail(ATTN_EINVAL, "workspace must be 16-byte aligned");
+        const uintptr_t w0 = reinterpret_cast<uintptr_t>(workspace), w1 = w0 + need;
+        const uint64_t kvb = uint64_t(B) * H * Tkv * d * 2, qb = uint64_t(B) * H * d * 2;
+        const uintptr_t ptrs[4] = {reinterpret_cast<uintptr_t>(q), reinterpret_cast<uintptr_t>(k),
+                                   reinterpret_cast<uintptr_t>(v), reinterpret_cast<uintptr_t>(o)};
+        const uint64_t lens[4] = {qb, kvb, kvb, qb};
+        for (int i = 0; i < 4; ++i)
+            if (w0 < ptrs[i] + lens[i] && ptrs[i] < w1) return fail(ATTN_EINVAL, "workspace overlaps a tensor");
+        if (lse) {
+            const uintptr_t l0 = reinterpret_cast<uintptr_t>(lse), l1 = l0 + uint64_t(B) * H * 4;
+            if (w0 < l1 && l0 < w1) return fail(ATTN_EINVAL, "workspace overlaps lse");
+        }
+    }
+    return run_decode(q, k, v, o, lse, B, H, Tkv, d, scale, splits, workspace, stream);
+}
+
+const char* attn_last_kernel(void) { return g_last_kernel.c_str(); }
+
+const char* attn_status_string(int status) {
+    if (status != ATTN_OK && status == g_detail_code && !g_detail.empty()) return g_detail.c_str();
+    return generic(status);
+}
+
+}  // extern "C"

@@ -1,0 +1,128 @@
+"""The C-ABI library: it loads, exports what include/attn.h declares, and its
+host-side validation rejects bad arguments before any HIP call.
+
+No test here launches a kernel: every call below fails validation, which
+runs before the library touches the HIP runtime, so these run without a GPU.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import io_aware_exact_amd as attn
+from io_aware_exact_amd.attn import SIGNATURES
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+EINVAL, EUNSUP, EWS = attn.ATTN_EINVAL, attn.ATTN_EUNSUPPORTED, attn.ATTN_EWORKSPACE
+
+# fake, 256-byte aligned "device" addresses far apart; never dereferenced
+Q, K, V, O, L, W = (0x10_0000_0000 * i for i in range(1, 7))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return attn.lib()
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
+
+
+def fwd(lib, **kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, H=3, Tq=64, Tkv=64, d=64, causal=0, scale=0.125, stream=None)
+    a.update(kw)
+    return lib.attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Tq"], a["Tkv"], a["d"],
+                        a["causal"], a["scale"], a["stream"])
+
+
+def fwd32(lib, **kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, H=3, Tq=64, Tkv=64, d=64, causal=0, scale=0.125, stream=None)
+    a.update(kw)
+    return lib.attn_fwd_f32(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Tq"], a["Tkv"], a["d"],
+                            a["causal"], a["scale"], a["stream"])
+
+
+def dec(lib, **kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, H=3, Tkv=100, d=128, scale=0.088, P=4, ws=W, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.attn_decode(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Tkv"], a["d"], a["scale"],
+                           a["P"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("call", [fwd, fwd32])
+@pytest.mark.parametrize("bad, want", [
+    (dict(q=None), "q is NULL"), (dict(k=None), "k is NULL"), (dict(v=None), "v is NULL"),
+    (dict(o=None), "o is NULL"),
+    (dict(B=0), "B must"), (dict(H=-1), "H must"), (dict(Tq=0), "Tq must"), (dict(Tkv=0), "Tkv must"),
+    (dict(d=0), "d must"),
+    (dict(causal=2), "causal must"),
+    (dict(scale=0.0), "scale"), (dict(scale=-0.5), "scale"), (dict(scale=float("nan")), "scale"),
+    (dict(scale=float("inf")), "scale"),
+    (dict(causal=1, Tq=65, Tkv=64), "Tq <= Tkv"),
+    (dict(q=Q + 2), "aligned"), (dict(o=O + 8), "aligned"), (dict(lse=L + 2), "aligned"),
+    (dict(o=Q + 4096), "o overlaps q"), (dict(lse=V + 256), "lse overlaps v"),
+])
+def test_invalid_arguments(lib, call, bad, want):
+    st = call(lib, **bad)
+    assert st == EINVAL
+    assert want in attn.attn_status_string(st)
+
+
+def test_unsupported_head_widths(lib):
+    assert fwd(lib, d=128) == EUNSUP and "d = 64" in attn.attn_status_string(EUNSUP)
+    assert fwd(lib, d=96, Tq=1) == EUNSUP
+    assert fwd32(lib, d=96) == EUNSUP
+    assert fwd32(lib, d=256) == EUNSUP
+    assert dec(lib, d=96) == EUNSUP
+
+
+def test_decode_arguments(lib):
+    assert dec(lib, P=0) == EINVAL and "num_splits" in attn.attn_status_string(EINVAL)
+    assert dec(lib, ws=None) == EWS and "NULL" in attn.attn_status_string(EWS)
+    need = attn.attn_decode_workspace_bytes(2, 3, 128, 4)
+    assert dec(lib, wsb=need - 1) == EWS and str(need) in attn.attn_status_string(EWS)
+    assert dec(lib, ws=W + 4) == EINVAL
+    assert dec(lib, ws=K + 64) == EINVAL and "overlaps" in attn.attn_status_string(EINVAL)
+    assert dec(lib, q=None) == EINVAL
+    assert dec(lib, scale=0.0) == EINVAL
+    assert dec(lib, Tkv=0) == EINVAL
+
+
+def test_workspace_size_formula():
+    assert attn.attn_decode_workspace_bytes(64, 32, 128, 16) == 64 * 32 * 16 * 130 * 4
+    assert attn.attn_decode_workspace_bytes(1, 1, 64, 1) == 0
+    assert attn.attn_decode_workspace_bytes(0, 1, 64, 4) == 0
+    assert attn.attn_decode_workspace_bytes(3, 5, 64, 7) == 3 * 5 * 7 * 66 * 4
+
+
+def test_status_strings(lib):
+    assert attn.attn_status_string(0) == "ok"
+    assert "unknown" in attn.attn_status_string(-99)
+    fwd(lib, B=0)
+    assert attn.attn_status_string(EINVAL) == "B must be >= 1"
+    assert attn.attn_status_string(attn.ATTN_EHIP) == "HIP runtime error"
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        attn.attn_fwd(x, x, x)
+    with pytest.raises(ValueError, match="shape"):
+        attn.attn_fwd(x, torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16), x)

@@ -1,0 +1,226 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle.
+
+Inputs are the seeded synthetic tensors of io_aware_exact_amd.inputs; the
+oracle sees exactly the values uploaded (bf16-rounded for bf16 cases).
+Tolerances: max-abs error on O <= 1e-5 for fp32 inputs and <= 2e-2 for bf16
+inputs; max-abs error on LSE <= 1e-3.  Small cases compare every output;
+the full-size workloads compare sampled rows the oracle computes one by one,
+in the same launch configuration the benchmark times.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import io_aware_exact_amd as attn
+import oracle
+from io_aware_exact_amd.inputs import WORKLOADS, Workload, make_qkv, to_f64
+
+pytestmark = [
+    pytest.mark.gpu,
+    pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU"),
+]
+
+TOL_O = {"f32": 1e-5, "bf16": 2e-2}
+TOL_LSE = 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(w: Workload, q, k, v, api=None):
+    dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
+    if api == "decode" or (api is None and w.Tq == 1 and w.num_splits > 1):
+        o, lse = attn.attn_decode(dq, dk, dv, scale=w.scale, num_splits=w.num_splits)
+        lse = lse[:, :, None]
+    elif w.dtype == "f32":
+        o, lse = attn.attn_fwd_f32(dq, dk, dv, causal=w.causal, scale=w.scale)
+    else:
+        o, lse = attn.attn_fwd(dq, dk, dv, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    return o, lse, attn.attn_last_kernel()
+
+
+def compare(w: Workload, o_gpu, lse_gpu, o_ref, lse_ref, what=""):
+    eo = float(np.abs(to_f64(o_gpu) - o_ref).max())
+    el = float(np.abs(to_f64(lse_gpu) - lse_ref).max())
+    say(f"  {w.name}{what}: max|dO|={eo:.3e} (tol {TOL_O[w.dtype]}), max|dLSE|={el:.3e}")
+    assert np.isfinite(to_f64(o_gpu)).all()
+    assert eo <= TOL_O[w.dtype], f"O error {eo}"
+    assert el <= TOL_LSE, f"LSE error {el}"
+    return eo, el
+
+
+def full_check(w: Workload, api=None):
+    say(f"case {w}")
+    q, k, v = make_qkv(w)
+    o, lse, kern = run_gpu(w, q, k, v, api)
+    say(f"  kernel {kern}")
+    o_ref, lse_ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), w.scale, w.causal)
+    return compare(w, o, lse, o_ref, lse_ref)
+
+
+# ------------------------------------------------------------ the named workloads
+
+def test_tiny_fp32_full():
+    full_check(WORKLOADS["tiny"])
+
+
+def test_gpt2_bf16_causal_full():
+    w = WORKLOADS["gpt2"]
+    full_check(w)
+    assert attn.attn_last_kernel().startswith("prefill_bf16_d64")
+
+
+def _sampled_rows(T, n, rng):
+    """First and last rows, rows around tile edges and a random spread."""
+    edge = [0, 1, 31, 32, 63, 64, 127, 128, 129, T // 2, T - 129, T - 128, T - 2, T - 1]
+    rnd = rng.choice(T, size=n, replace=False).tolist()
+    return np.array(sorted(set(r for r in edge + rnd if 0 <= r < T)))
+
+
+@pytest.mark.parametrize("name", ["mid", "mid_causal", "long"])
+def test_prefill_full_size_sampled(name):
+    w = WORKLOADS[name]
+    say(f"case {w} (sampled rows)")
+    q, k, v = make_qkv(w)
+    o, lse, kern = run_gpu(w, q, k, v)
+    say(f"  kernel {kern}")
+    rng = np.random.default_rng(1000 + w.seed)
+    heads = [(0, 0), (w.B - 1, w.H - 1), (w.B // 2, w.H // 3)]
+    for b, h in heads:
+        rows = _sampled_rows(w.Tq, 48, rng)
+        o_ref, lse_ref = oracle.attention(to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]), w.scale, w.causal,
+                                          rows=rows)
+        compare(w, o[b, h][torch.from_numpy(rows).cuda()], lse[b, h][torch.from_numpy(rows).cuda()],
+                o_ref, lse_ref, what=f"[b={b},h={h}, {rows.size} rows]")
+
+
+def test_decode_full_size_sampled():
+    w = WORKLOADS["decode"]
+    say(f"case {w} (sampled heads)")
+    q, k, v = make_qkv(w)
+    o, lse, kern = run_gpu(w, q, k, v)
+    say(f"  kernel {kern}")
+    assert "combine" in kern
+    rng = np.random.default_rng(77)
+    picks = [(0, 0), (w.B - 1, w.H - 1)] + [(int(b), int(h)) for b, h in
+                                            zip(rng.integers(0, w.B, 14), rng.integers(0, w.H, 14))]
+    for b, h in picks:
+        o_ref, lse_ref = oracle.attention(to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]), w.scale)
+        compare(w, o[b, h], lse[b, h], o_ref, lse_ref, what=f"[b={b},h={h}]")
+    # the split result against the unsplit kernel on the same inputs
+    o1, lse1 = attn.attn_fwd(q.cuda(), k.cuda(), v.cuda(), scale=w.scale)
+    torch.cuda.synchronize()
+    d = float((o1.float() - o.float()).abs().max())
+    say(f"  split vs unsplit max|dO|={d:.3e}")
+    assert d <= 2e-2
+
+
+# ------------------------------------------------------------ shapes and edges
+
+PREFILL_CASES = [
+    # B, H, Tq, Tkv, causal
+    (1, 2, 200, 200, False),
+    (1, 2, 200, 200, True),
+    (2, 3, 129, 129, True),
+    (1, 1, 384, 384, True),
+    (1, 2, 100, 300, True),     # bottom-right causal, Tq < Tkv
+    (1, 2, 100, 300, False),
+    (1, 1, 257, 1000, False),
+    (2, 2, 64, 64, True),
+    (1, 1, 2, 2, True),
+    (1, 3, 5, 1, False),        # one key
+    (1, 1, 300, 17, False),     # fewer keys than a block
+    (1, 1, 33, 700, True),
+    (3, 1, 1000, 1000, True),
+]
+
+
+@pytest.mark.parametrize("B,H,Tq,Tkv,causal", PREFILL_CASES)
+def test_prefill_bf16_shapes(B, H, Tq, Tkv, causal):
+    full_check(Workload(f"bf16[{B},{H},{Tq},{Tkv},{'c' if causal else 'n'}]", B, H, Tq, Tkv, 64, "bf16", causal,
+                        seed=11 + Tq + Tkv))
+
+
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("Tq,Tkv,causal", [(256, 256, False), (100, 100, True), (70, 333, True), (1, 65, False)])
+def test_prefill_fp32_shapes(d, Tq, Tkv, causal):
+    full_check(Workload(f"f32[d={d},{Tq},{Tkv},{'c' if causal else 'n'}]", 2, 2, Tq, Tkv, d, "f32", causal,
+                        seed=5 + d + Tq))
+
+
+def test_fp32_scores_spread():
+    w = WORKLOADS["tiny"].with_(name="tiny_k3", k_factor=3.0)
+    full_check(w)
+
+
+@pytest.mark.parametrize("B,H,Tkv,d,splits", [
+    (2, 3, 1000, 128, 16), (3, 2, 77, 64, 3), (1, 1, 1, 128, 16), (4, 4, 8192, 64, 16),
+    (2, 2, 512, 128, 1), (2, 2, 513, 128, 2), (1, 2, 40, 128, 45), (5, 3, 4097, 128, 7),
+])
+def test_decode_shapes(B, H, Tkv, d, splits):
+    full_check(Workload(f"decode[{B},{H},{Tkv},d={d},P={splits}]", B, H, 1, Tkv, d, "bf16", False,
+                        seed=3 + Tkv, num_splits=splits), api="decode")
+    assert ("combine" in attn.attn_last_kernel()) == (min(splits, Tkv) > 1)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_single_query_through_attn_fwd(d):
+    w = Workload(f"fwd_tq1[d={d}]", 3, 4, 1, 2049, d, "bf16", True, seed=21)
+    full_check(w)
+    assert attn.attn_last_kernel().startswith("decode_bf16")
+
+
+def test_spread_scores_bf16():
+    w = Workload("bf16_k3", 1, 4, 512, 512, 64, "bf16", False, seed=8, k_factor=3.0)
+    full_check(w)
+    full_check(w.with_(causal=True, name="bf16_k3_causal"))
+
+
+def test_lse_optional_and_outputs_in_place():
+    w = Workload("inplace", 1, 2, 130, 130, 64, "bf16", True, seed=4)
+    q, k, v = [t.cuda() for t in make_qkv(w)]
+    o_ref, lse_ref = attn.attn_fwd(q, k, v, causal=True)
+    out = torch.full_like(q, float("nan"))
+    o2 = attn.attn_fwd(q, k, v, causal=True, out=out, return_lse=False)
+    torch.cuda.synchronize()
+    assert o2.data_ptr() == out.data_ptr()
+    assert torch.equal(o2, o_ref)
+
+
+def test_deterministic_across_runs():
+    w = WORKLOADS["gpt2"].with_(B=1, H=4)
+    q, k, v = [t.cuda() for t in make_qkv(w)]
+    o1, l1 = attn.attn_fwd(q, k, v, causal=True)
+    o2, l2 = attn.attn_fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_misaligned_view_rejected_before_launch():
+    base = torch.zeros(1 * 1 * 64 * 64 + 1, dtype=torch.bfloat16, device="cuda")
+    q = base[1:].view(1, 1, 64, 64)
+    k = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="aligned"):
+        attn.attn_fwd(q, k, k)
+
+
+def test_no_device_allocation_during_call():
+    """The score matrix never exists: a prefill call allocates nothing on the
+    device beyond the caller's O and LSE (the library has no allocator)."""
+    w = WORKLOADS["long"].with_(H=2)
+    q, k, v = [t.cuda() for t in make_qkv(w)]
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    attn.attn_fwd(q, k, v, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    # one T x T fp32 score matrix per head would be 1 GiB here
+    assert free0 - free1 < (1 << 20)
