@@ -113,6 +113,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
         return run_decode(q, k, v, o, lse, B, H, Tkv, d, scale, 1, nullptr, stream);
     }
     if (d != 64) return fail(ATTN_EUNSUPPORTED, "bf16 prefill supports d = 64");
+    if (!attn::prefill_bf16_fits(Tkv)) return fail(ATTN_EUNSUPPORTED, "bf16 prefill supports Tkv*d*2 < 2^31 bytes per head");
     if (double(B) * H * ((Tq + 127) / 128) > 2147483647.0) return fail(ATTN_EINVAL, "grid too large");
     attn::PrefillArgs a{q, k, v, o, lse, B, H, Tq, Tkv, d, causal != 0, float(double(scale) * kLog2e)};
     const char* name = nullptr;

@@ -99,8 +99,7 @@ void decode_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
             float acc = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, kw[u][i]),
-                                                      __builtin_bit_cast(bf16x2_t, qw[i]), acc, false);
+                acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kw[u][i]), as_bf16x2(qw[i]), acc, false);
             acc = row_sum<LPK>(acc);
             const long long key = base + (long long)(wave * UNROLL + u) * KPW + kr;
             s[u] = (key < hi) ? acc * c : kNegInf;

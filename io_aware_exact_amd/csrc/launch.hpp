@@ -31,6 +31,7 @@ struct DecodeArgs {
 };
 
 hipError_t launch_prefill_bf16_d64(const PrefillArgs& a, hipStream_t stream, const char** name);
+bool prefill_bf16_fits(int Tkv);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream, const char** name);
 bool prefill_f32_supports(int d);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream, const char** name);

@@ -5,32 +5,42 @@
 // Tiling the Score Matrix Without Materializing It", section "What has to
 // stay in fast memory"; "FlashAttention IO-aware tiling lab", kernel phases
 // load Q / score a K tile / update the online softmax / accumulate V / write O
-// once).  Per key block:
+// once).  Per key block j:
 //
-//   S^T = K_j Q^T        v_mfma_f32_32x32x16_bf16, fp32 accumulate
-//   m'  = max(m, rowmax S * c)                       (c = scale * log2 e)
-//   P   = exp2(S * c - m'),  l = exp2(m - m') l + rowsum P
-//   O^T = exp2(m - m') O^T + V_j^T bf16(P)^T          (mfma again)
+//   S^T = K_j Q^T                       v_mfma_f32_32x32x16_bf16, fp32 accumulate
+//   P   = exp2(S * c - m)               c = scale * log2 e, m = reference max
+//   l  += rowsum P (fp32);  O^T += V_j^T bf16(P)^T      (mfma again)
 //
-// which is the running-max / running-sum recurrence of "IO-Aware Attention",
-// section "Softmax over blocks, exactly", written in base 2.  O is divided by
-// l once at the end and the row's log-sum-exp is written beside it.
+// This is the running-max / running-sum recurrence of "IO-Aware Attention",
+// section "Softmax over blocks, exactly", in base 2, with one liberty the
+// recurrence allows: the reference m is only raised when a block would
+// otherwise produce large terms.  The final O / l and m + log2 l do not depend
+// on which reference was used (the rescaling factors telescope), so any m not
+// far below the running maximum gives the exact result; m is raised (and l, O
+// rescaled by exp2(m_old - m_new)) whenever a row's block sum exceeds 2^16 or
+// is not finite, which bounds every term by 2^16 and keeps fp32 far from
+// overflow.  Blocks therefore cost no row-max in the common case: softmax work
+// is one FMA, one exp2 and one add per score and a bf16 pack per pair -- the
+// VALU budget is what limits a d = 64 head on CDNA4, since each score carries
+// only 4*64 MFMA flops.  (The row sum stays fp32: a sum of the bf16-rounded
+// terms would cost the log-sum-exp up to 2^-9 relative on short rows.)
 //
 // Layout choices for CDNA4:
 // * Computing the transposed products puts one query row in each lane (lane
-//   l and l+32 hold the two halves of row l % 32), so row max / row sum are
-//   lane-local plus one exchange with lane l ^ 32, the softmax rescale is a
-//   per-lane scalar multiply, and the fp32 P accumulator of the first product
-//   is already the B operand of the second (only a bf16 pack in between).
+//   l and l+32 hold the two halves of row l % 32), so row sums are lane-local
+//   plus one v_permlane32_swap, the softmax rescale is a per-lane scalar, and
+//   the fp32 accumulator of the first product is already the B operand of the
+//   second (only a bf16 pack in between).
 // * Q stays in VGPRs for the whole key loop (16 VGPRs per lane).
 // * K blocks are staged row-major in LDS (row pitch 144 B); V blocks are
 //   transposed in registers on the way in and staged as V^T (row pitch 136 B)
 //   so the PV operand is two 8-byte LDS reads per lane.  Both are double
-//   buffered: block j+1 is fetched from HBM into registers while block j is
-//   multiplied, then written to the other LDS buffer.
+//   buffered: block j+1 is fetched into registers by buffer loads (whose range
+//   check zero-fills the ragged end) while block j is multiplied, then written
+//   to the other LDS buffer; one barrier per block.
 // * Causal: the key loop stops at the tile's diagonal block; element masks
-//   are applied only on blocks that cross the diagonal or the ragged end, and
-//   a wave whose rows all lie above a block skips its math for that block.
+//   are applied only on blocks that cross a wave's diagonal or the ragged end,
+//   and a wave whose rows all lie above a block skips its math for that block.
 // * Tiles are launched heaviest-first (last query tiles first) and the
 //   linear block id keeps every tile of one (batch, head) on one XCD when the
 //   number of heads is a multiple of 8.
@@ -44,9 +54,10 @@ constexpr int D = 64;
 constexpr int BK = 64;
 constexpr int KPITCH = 72;   // bf16 elements per K row in LDS (64 + 8 pad)
 constexpr int VPITCH = 68;   // bf16 elements per V^T row in LDS (64 + 4 pad)
+constexpr float kSumLimit = 65536.0f;        // 2^16: largest block row sum kept without raising m
 
 template <int WAVES, bool CAUSAL>
-__global__ __launch_bounds__(WAVES * 64)
+__global__ __launch_bounds__(WAVES * 64, 2)
 void prefill_bf16_d64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                              const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                              float* __restrict__ LSE, int Tq, int Tkv, int BH, int nqt, float c) {
@@ -74,6 +85,8 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __r
 
     const size_t qbase = (size_t)bh * Tq * D;
     const size_t kvbase = (size_t)bh * Tkv * D;
+    const uint16_t* Kh = K + kvbase;
+    const uint16_t* Vh = V + kvbase;
 
     // ---- Q fragment: row q0 + 32*wave + ln, d = 16t + 8hf + (0..7) ----
     const int qrow = q0 + wave * 32 + ln;
@@ -91,60 +104,56 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __r
     const int nblk = (kend + BK - 1) / BK;
     const int wq_first = q0 + wave * 32;       // this wave's first / last query row
     const int wq_last = wq_first + 31;
+    const int lim = CAUSAL ? min(Tkv - 1, qrow + off) : (Tkv - 1);   // last key this row may see
 
-    // ---- global -> register staging of one K/V block ----
+    // ---- per-thread constant offsets of the block loads and LDS stores ----
+    uint32_t k_goff[KCH], k_soff[KCH];
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+        const int ch = tid + i * NT;
+        const int row = ch >> 3, col = (ch & 7) * 8;
+        k_goff[i] = (uint32_t)(row * D + col) * 2u;
+        k_soff[i] = (uint32_t)(row * KPITCH + col);
+    }
+    uint32_t v_goff[VUN], v_soff[VUN];
+#pragma unroll
+    for (int u = 0; u < VUN; ++u) {
+        const int un = tid + u * NT;
+        const int kg = un >> 4, dg = un & 15;
+        v_goff[u] = (uint32_t)((4 * kg) * D + 4 * dg) * 2u;
+        v_soff[u] = (uint32_t)((4 * dg) * VPITCH + 4 * kg);
+    }
+
     u32x4_t kreg[KCH];
     u32x2_t vreg[VUN][4];
 
     auto fetch = [&](int j) {
         const int kb = j * BK;
+        const uint32_t bytes = (uint32_t)(Tkv - kb) * (uint32_t)(D * 2);
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)kb * D, bytes);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (size_t)kb * D, bytes);
 #pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int ch = tid + i * NT;
-            const int row = ch >> 3, col = (ch & 7) * 8;
-            if (kb + row < Tkv)
-                kreg[i] = *reinterpret_cast<const u32x4_t*>(K + kvbase + (size_t)(kb + row) * D + col);
-            else
-                kreg[i] = u32x4_t{0, 0, 0, 0};
-        }
+        for (int i = 0; i < KCH; ++i) kreg[i] = buffer_load_b128(rk, k_goff[i]);
 #pragma unroll
-        for (int u = 0; u < VUN; ++u) {
-            const int un = tid + u * NT;
-            const int kg = un >> 4, dg = un & 15;
+        for (int u = 0; u < VUN; ++u)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = kb + 4 * kg + i;
-                if (row < Tkv)
-                    vreg[u][i] = *reinterpret_cast<const u32x2_t*>(V + kvbase + (size_t)row * D + 4 * dg);
-                else
-                    vreg[u][i] = u32x2_t{0, 0};
-            }
-        }
+            for (int i = 0; i < 4; ++i) vreg[u][i] = buffer_load_b64(rv, v_goff[u] + (uint32_t)(i * D * 2));
     };
 
     auto stage = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int ch = tid + i * NT;
-            const int row = ch >> 3, col = (ch & 7) * 8;
-            *reinterpret_cast<u32x4_t*>(&Ks[buf][row * KPITCH + col]) = kreg[i];
-        }
+        for (int i = 0; i < KCH; ++i) *reinterpret_cast<u32x4_t*>(&Ks[buf][k_soff[i]]) = kreg[i];
 #pragma unroll
         for (int u = 0; u < VUN; ++u) {
-            const int un = tid + u * NT;
-            const int kg = un >> 4, dg = un & 15;
-            // vreg[u][i] holds V[4kg+i][4dg .. 4dg+3]; write column 4dg+cc as
-            // the four keys 4kg .. 4kg+3 of row 4dg+cc of V^T.
+            // vreg[u][i] holds V[4kg+i][4dg .. 4dg+3]; row 4dg+cc of V^T gets
+            // the four keys 4kg .. 4kg+3 of column 4dg+cc.
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) {
-                uint32_t e[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t w = (cc < 2) ? vreg[u][i][0] : vreg[u][i][1];
-                    e[i] = (cc & 1) ? (w >> 16) : (w & 0xffffu);
-                }
-                u32x2_t out = {e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
-                *reinterpret_cast<u32x2_t*>(&Vt[buf][(4 * dg + cc) * VPITCH + 4 * kg]) = out;
+                const int w = cc >> 1;
+                const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
+                const u32x2_t out = {__builtin_amdgcn_perm(vreg[u][1][w], vreg[u][0][w], sel),
+                                     __builtin_amdgcn_perm(vreg[u][3][w], vreg[u][2][w], sel)};
+                *reinterpret_cast<u32x2_t*>(&Vt[buf][v_soff[u] + cc * VPITCH]) = out;
             }
         }
     };
@@ -154,90 +163,114 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __r
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
-    float m = kNegInf;   // running max of S * c (log2 units)
-    float l = 0.f;       // this lane's share of the running sum
+    float m = kNegInf;   // reference max of S * c (log2 units), raised only when needed
+    float l = 0.f;       // this lane's share of the running sum (relative to m)
+
+    // One key block for this wave.  MASK applies the causal / ragged element mask.
+    auto step = [&](int buf, int kb, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        f32x16_t s[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const bf16x8_t a =
+                    *reinterpret_cast<const bf16x8_t*>(&Ks[buf][(32 * kt + ln) * KPITCH + 16 * t + 8 * hf]);
+                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kt], 0, 0, 0);
+            }
+        }
+        if constexpr (MASK) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kb + 32 * kt + 8 * (r >> 2) + 4 * hf + (r & 3);
+                    if (key > lim) s[kt][r] = kNegInf;
+                }
+        }
+        // exponentials against the current reference; packed to bf16 pairs
+        uint32_t pw[16];
+        float rs = 0.f;
+        auto exponentiate = [&](float mref) {
+            rs = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int kt = i >> 3, r = 2 * (i & 7);
+                const float p0 = fast_exp2(__builtin_fmaf(s[kt][r], c, -mref));
+                const float p1 = fast_exp2(__builtin_fmaf(s[kt][r + 1], c, -mref));
+                pw[i] = pack_bf16x2(p0, p1);
+                rs += p0 + p1;
+            }
+        };
+        exponentiate(m);
+        const float row = half_swap_sum(rs);
+        if (__builtin_amdgcn_ballot_w64(!(row <= kSumLimit)) != 0) {
+            // raise the reference to the true running max and rescale
+            float mx = kNegInf;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+            mx = half_swap_max(mx);
+            const float m_new = fmaxf(m, mx * c);
+            const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+            const float alpha = fast_exp2(m - m_use);
+            l *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+            m = m_new;
+            exponentiate(m_use);
+        }
+        l += rs;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const u32x4_t pv = {pw[4 * st], pw[4 * st + 1], pw[4 * st + 2], pw[4 * st + 3]};
+            const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pv);
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt) {
+                const uint16_t* vrow = &Vt[buf][(32 * dt + ln) * VPITCH + 16 * st + 4 * hf];
+                const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow);
+                const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + 8);
+                const u32x4_t aw = {lo[0], lo[1], hi[0], hi[1]};
+                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, aw), pb, oacc[dt],
+                                                                   0, 0, 0);
+            }
+        }
+    };
+
+    // Blocks [0, nfull) need no element mask for any row of the tile: they lie
+    // inside the key range and, for causal, left of every row's diagonal.
+    // Blocks [nfull, nblk) may be masked (diagonal or ragged end) or, for a
+    // wave whose rows all precede them, skipped.
+    const int nfull = CAUSAL ? min(Tkv / BK, (q0 + off + 1) / BK) : Tkv / BK;
 
     fetch(0);
     stage(0);
     __syncthreads();
 
-    for (int j = 0; j < nblk; ++j) {
+    int j = 0;
+    for (; j < nfull; ++j) {
+        const int buf = j & 1;
+        if (j + 1 < nblk) fetch(j + 1);
+        step(buf, j * BK, std::false_type{});
+        if (j + 1 < nblk) stage(buf ^ 1);
+        __syncthreads();
+    }
+    for (; j < nblk; ++j) {
         const int buf = j & 1;
         if (j + 1 < nblk) fetch(j + 1);
         const int kb = j * BK;
-        const bool active = !CAUSAL || (kb <= wq_last + off);
-        if (active) {
-            f32x16_t s[2];
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&Ks[buf][(32 * kt + ln) * KPITCH + 16 * t + 8 * hf]);
-                    s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kt], 0, 0, 0);
-                }
-            }
-            // element masks: ragged end of the keys, and the causal diagonal
-            const bool ragged = kb + BK > Tkv;
-            const bool diag = CAUSAL && (kb + BK - 1 > wq_first + off);
-            if (ragged || diag) {
-                const int lim = CAUSAL ? min(Tkv - 1, qrow + off) : (Tkv - 1);
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = kb + 32 * kt + 8 * (r >> 2) + 4 * hf + (r & 3);
-                        if (key > lim) s[kt][r] = kNegInf;
-                    }
-            }
-            float mx = s[0][0];
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-            mx = fmaxf(mx, xor_lane(mx, 32));
-            const float m_new = fmaxf(m, mx * c);
-            const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-            const float alpha = fast_exp2(m - m_use);
-            float psum = 0.f;
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = fast_exp2(__builtin_fmaf(s[kt][r], c, -m_use));
-                    s[kt][r] = p;
-                    psum += p;
-                }
-            l = l * alpha + psum;
-            m = m_new;
-#pragma unroll
-            for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-#pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                const int kt = st >> 1, r0 = 8 * (st & 1);
-                u32x4_t pw;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) pw[i] = pack_bf16x2(s[kt][r0 + 2 * i], s[kt][r0 + 2 * i + 1]);
-                const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
-#pragma unroll
-                for (int dt = 0; dt < 2; ++dt) {
-                    const uint16_t* vrow = &Vt[buf][(32 * dt + ln) * VPITCH + 16 * st + 4 * hf];
-                    const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow);
-                    const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + 8);
-                    const u32x4_t aw = {lo[0], lo[1], hi[0], hi[1]};
-                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, aw), pb, oacc[dt], 0, 0, 0);
-                }
-            }
-        }
+        if (!CAUSAL || kb <= wq_last + off) step(buf, kb, std::true_type{});
         if (j + 1 < nblk) stage(buf ^ 1);
         __syncthreads();
     }
 
     // ---- epilogue: divide once, write O (bf16) and LSE (fp32) ----
-    const float lsum = l + xor_lane(l, 32);
+    const float lsum = half_swap_sum(l);
     if (qrow < Tq) {
         const float inv = 1.0f / lsum;
         uint16_t* orow = O + qbase + (size_t)qrow * D;
@@ -268,6 +301,11 @@ hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+bool prefill_bf16_fits(int Tkv) {
+    // buffer-load ranges are 32-bit byte counts per (batch, head)
+    return (long long)Tkv * D * 2 < (1LL << 31);
+}
 
 hipError_t launch_prefill_bf16_d64(const PrefillArgs& a, hipStream_t stream, const char** name) {
     if (a.causal) {
