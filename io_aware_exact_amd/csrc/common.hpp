@@ -62,6 +62,44 @@ __device__ __forceinline__ u32x2_t buffer_load_b64(__amdgpu_buffer_rsrc_t r, uin
     return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+// 16 bytes per lane from the buffer straight into LDS: lane i's bytes land at
+// lds_base + 16 * i (lds_base is wave-uniform); out-of-range offsets write zeros.
+__device__ __forceinline__ void buffer_load_lds_b128(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 16, (int)voff, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) (other counters untouched); gfx9 encoding of the immediate.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N & 0x30) << 10) | (0x7 << 4) | (0xF << 8));
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// (i % 4) of the 8-byte pieces addressed by lanes 4r + i/4, r = 0..3.
+// Issued as inline asm because the compiler would otherwise wait for every
+// outstanding LDS DMA before it (it cannot see that the rings' stages do not
+// overlap); the caller must pass the results through lgkm_wait_* before use.
+template <int OFF>
+__device__ __forceinline__ u32x2_t lds_read_tr16_b64(uint32_t addr) {
+    u32x2_t v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+// s_waitcnt lgkmcnt(0) that the given registers flow through, so nothing that
+// reads them can be scheduled before the wait.
+__device__ __forceinline__ void lgkm_wait_4(u32x2_t& a, u32x2_t& b, u32x2_t& c, u32x2_t& d) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+
 // DPP row-local exchanges: lanes are paired within rows of 16.
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {

@@ -32,12 +32,16 @@
 //   the fp32 accumulator of the first product is already the B operand of the
 //   second (only a bf16 pack in between).
 // * Q stays in VGPRs for the whole key loop (16 VGPRs per lane).
-// * K blocks are staged row-major in LDS (row pitch 144 B); V blocks are
-//   transposed in registers on the way in and staged as V^T (row pitch 136 B)
-//   so the PV operand is two 8-byte LDS reads per lane.  Both are double
-//   buffered: block j+1 is fetched into registers by buffer loads (whose range
-//   check zero-fills the ragged end) while block j is multiplied, then written
-//   to the other LDS buffer; one barrier per block.
+// * K and V blocks go from HBM straight into an NS-stage LDS ring with
+//   buffer_load ... lds (no staging registers, no LDS store instructions;
+//   the buffer range check zero-fills the ragged end).  Rows keep their
+//   natural 128-byte layout with the 16-byte chunks XOR-swizzled per row, so
+//   the K operand reads (ds_read_b128) and the V operand reads are free of
+//   bank conflicts.  V is read with ds_read_b64_tr_b16, which hands every
+//   lane four consecutive keys of one column: exactly the operand layout of
+//   the PV product, without transposing V anywhere.
+// * One barrier per block: it publishes block j (waited for with vmcnt) and
+//   frees the stage block j+NS-1 is then loaded into.
 // * Causal: the key loop stops at the tile's diagonal block; element masks
 //   are applied only on blocks that cross a wave's diagonal or the ragged end,
 //   and a wave whose rows all lie above a block skips its math for that block.
@@ -52,23 +56,24 @@ namespace {
 
 constexpr int D = 64;
 constexpr int BK = 64;
-constexpr int KPITCH = 72;   // bf16 elements per K row in LDS (64 + 8 pad)
-constexpr int VPITCH = 68;   // bf16 elements per V^T row in LDS (64 + 4 pad)
-constexpr float kSumLimit = 65536.0f;        // 2^16: largest block row sum kept without raising m
+constexpr int ROWB = D * 2;                   // bytes per K/V row
+constexpr int TILEB = BK * ROWB;              // bytes per K (or V) block: 8 KiB
+constexpr float kSumLimit = 65536.0f;         // 2^16: largest block row sum kept without raising m
 
-template <int WAVES, bool CAUSAL>
+// 16-byte chunk swizzles (chunk index within a 128-byte row).
+__device__ __forceinline__ int swz_k(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz_v(int row) { return ((row >> 1) & 1) << 2; }
+
+template <int WAVES, int NS, bool CAUSAL>
 __global__ __launch_bounds__(WAVES * 64, 2)
 void prefill_bf16_d64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                              const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                              float* __restrict__ LSE, int Tq, int Tkv, int BH, int nqt, float c) {
     constexpr int BQ = WAVES * 32;
-    constexpr int NT = WAVES * 64;
-    static_assert(512 % NT == 0 && 256 % NT == 0, "thread count must divide the tile loads");
-    constexpr int KCH = 512 / NT;   // 16-byte K chunks per thread per block
-    constexpr int VUN = 256 / NT;   // 4x4 V sub-blocks per thread per block
+    static_assert(8 % WAVES == 0, "row groups of a block must split evenly over the waves");
+    constexpr int LI = 8 / WAVES;             // 1 KiB load instructions per wave per operand per block
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BK * KPITCH];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VPITCH];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[NS][2][TILEB];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -106,57 +111,52 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __r
     const int wq_last = wq_first + 31;
     const int lim = CAUSAL ? min(Tkv - 1, qrow + off) : (Tkv - 1);   // last key this row may see
 
-    // ---- per-thread constant offsets of the block loads and LDS stores ----
-    uint32_t k_goff[KCH], k_soff[KCH];
+    // ---- DMA loads: wave w moves row groups g = w + WAVES*i (8 rows = 1 KiB each) ----
+    uint32_t k_voff[LI], v_voff[LI];
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-        const int ch = tid + i * NT;
-        const int row = ch >> 3, col = (ch & 7) * 8;
-        k_goff[i] = (uint32_t)(row * D + col) * 2u;
-        k_soff[i] = (uint32_t)(row * KPITCH + col);
+    for (int i = 0; i < LI; ++i) {
+        const int g = wave + WAVES * i;
+        const int row = 8 * g + (lane >> 3);
+        const int slot = lane & 7;            // the chunk position this lane fills in LDS
+        k_voff[i] = (uint32_t)(row * ROWB + ((slot ^ swz_k(row)) << 4));
+        v_voff[i] = (uint32_t)(row * ROWB + ((slot ^ swz_v(row)) << 4));
     }
-    uint32_t v_goff[VUN], v_soff[VUN];
-#pragma unroll
-    for (int u = 0; u < VUN; ++u) {
-        const int un = tid + u * NT;
-        const int kg = un >> 4, dg = un & 15;
-        v_goff[u] = (uint32_t)((4 * kg) * D + 4 * dg) * 2u;
-        v_soff[u] = (uint32_t)((4 * dg) * VPITCH + 4 * kg);
-    }
-
-    u32x4_t kreg[KCH];
-    u32x2_t vreg[VUN][4];
-
-    auto fetch = [&](int j) {
+    // Block j goes to stage j % NS.  Blocks past the end still issue (empty
+    // range, no memory traffic) so that every wave's vmcnt stays uniform.
+    auto issue = [&](int j) {
         const int kb = j * BK;
-        const uint32_t bytes = (uint32_t)(Tkv - kb) * (uint32_t)(D * 2);
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)kb * D, bytes);
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (size_t)kb * D, bytes);
+        const bool live = kb < Tkv;
+        const uint32_t bytes = live ? (uint32_t)(Tkv - kb) * (uint32_t)ROWB : 0u;
+        const size_t eoff = live ? (size_t)kb * D : 0;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + eoff, bytes);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + eoff, bytes);
+        uint8_t* st = &ring[j % NS][0][0];
 #pragma unroll
-        for (int i = 0; i < KCH; ++i) kreg[i] = buffer_load_b128(rk, k_goff[i]);
-#pragma unroll
-        for (int u = 0; u < VUN; ++u)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) vreg[u][i] = buffer_load_b64(rv, v_goff[u] + (uint32_t)(i * D * 2));
-    };
-
-    auto stage = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < KCH; ++i) *reinterpret_cast<u32x4_t*>(&Ks[buf][k_soff[i]]) = kreg[i];
-#pragma unroll
-        for (int u = 0; u < VUN; ++u) {
-            // vreg[u][i] holds V[4kg+i][4dg .. 4dg+3]; row 4dg+cc of V^T gets
-            // the four keys 4kg .. 4kg+3 of column 4dg+cc.
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-                const int w = cc >> 1;
-                const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
-                const u32x2_t out = {__builtin_amdgcn_perm(vreg[u][1][w], vreg[u][0][w], sel),
-                                     __builtin_amdgcn_perm(vreg[u][3][w], vreg[u][2][w], sel)};
-                *reinterpret_cast<u32x2_t*>(&Vt[buf][v_soff[u] + cc * VPITCH]) = out;
-            }
+        for (int i = 0; i < LI; ++i) {
+            const int g = wave + WAVES * i;
+            buffer_load_lds_b128(rk, k_voff[i], st + g * 1024);
+            buffer_load_lds_b128(rv, v_voff[i], st + TILEB + g * 1024);
         }
     };
+
+    // ---- per-lane LDS read offsets (within a stage) ----
+    // K operand of step t: row 32kt + ln, chunk 2t + hf (kt adds 32 rows = 4 KiB).
+    uint32_t k_roff[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) k_roff[t] = (uint32_t)(ln * ROWB + (((2 * t + hf) ^ swz_k(ln)) << 4));
+    // V operand (transposed read) of step st, d-tile dt: lane group G = lane / 16,
+    // j = lane % 16 addresses row 16st + 4(G/2) + j/4 (+8 for the second half),
+    // columns 32dt + 16(G%2) + 4(j%4) .. +3 (st adds 2 KiB).
+    uint32_t v_roff[2];
+    {
+        const int G = lane >> 4, jj = lane & 15;
+        const int row = 4 * (G >> 1) + (jj >> 2);
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+            const int col = 32 * dt + 16 * (G & 1) + 4 * (jj & 3);
+            v_roff[dt] = (uint32_t)(row * ROWB + ((((col >> 3) ^ swz_v(row)) << 4) | ((col & 4) << 1)));
+        }
+    }
 
     f32x16_t oacc[2];
 #pragma unroll
@@ -167,8 +167,9 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __r
     float l = 0.f;       // this lane's share of the running sum (relative to m)
 
     // One key block for this wave.  MASK applies the causal / ragged element mask.
-    auto step = [&](int buf, int kb, auto mask_tag) {
+    auto step = [&](const uint8_t* kst, int kb, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
+        const uint8_t* vst = kst + TILEB;
         f32x16_t s[2];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
@@ -176,8 +177,7 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __r
             for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const bf16x8_t a =
-                    *reinterpret_cast<const bf16x8_t*>(&Ks[buf][(32 * kt + ln) * KPITCH + 16 * t + 8 * hf]);
+                const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kst + k_roff[t] + kt * 32 * ROWB);
                 s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kt], 0, 0, 0);
             }
         }
@@ -226,20 +226,27 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __r
             exponentiate(m_use);
         }
         l += rs;
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
+        const uint32_t va0 = lds_addr(vst) + v_roff[0];
+        const uint32_t va1 = lds_addr(vst) + v_roff[1];
+        auto pv_step = [&](auto st_tag) {
+            constexpr int st = decltype(st_tag)::value;
+            constexpr int o = st * 16 * ROWB;
+            u32x2_t lo0 = lds_read_tr16_b64<o>(va0);
+            u32x2_t hi0 = lds_read_tr16_b64<o + 8 * ROWB>(va0);
+            u32x2_t lo1 = lds_read_tr16_b64<o>(va1);
+            u32x2_t hi1 = lds_read_tr16_b64<o + 8 * ROWB>(va1);
+            lgkm_wait_4(lo0, hi0, lo1, hi1);
             const u32x4_t pv = {pw[4 * st], pw[4 * st + 1], pw[4 * st + 2], pw[4 * st + 3]};
             const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pv);
-#pragma unroll
-            for (int dt = 0; dt < 2; ++dt) {
-                const uint16_t* vrow = &Vt[buf][(32 * dt + ln) * VPITCH + 16 * st + 4 * hf];
-                const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow);
-                const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + 8);
-                const u32x4_t aw = {lo[0], lo[1], hi[0], hi[1]};
-                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, aw), pb, oacc[dt],
-                                                                   0, 0, 0);
-            }
-        }
+            const u32x4_t a0 = {lo0[0], lo0[1], hi0[0], hi0[1]};
+            const u32x4_t a1 = {lo1[0], lo1[1], hi1[0], hi1[1]};
+            oacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a0), pb, oacc[0], 0, 0, 0);
+            oacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a1), pb, oacc[1], 0, 0, 0);
+        };
+        pv_step(std::integral_constant<int, 0>{});
+        pv_step(std::integral_constant<int, 1>{});
+        pv_step(std::integral_constant<int, 2>{});
+        pv_step(std::integral_constant<int, 3>{});
     };
 
     // Blocks [0, nfull) need no element mask for any row of the tile: they lie
@@ -248,26 +255,24 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __r
     // wave whose rows all precede them, skipped.
     const int nfull = CAUSAL ? min(Tkv / BK, (q0 + off + 1) / BK) : Tkv / BK;
 
-    fetch(0);
-    stage(0);
-    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j) issue(j);
 
     int j = 0;
     for (; j < nfull; ++j) {
-        const int buf = j & 1;
-        if (j + 1 < nblk) fetch(j + 1);
-        step(buf, j * BK, std::false_type{});
-        if (j + 1 < nblk) stage(buf ^ 1);
-        __syncthreads();
+        wait_vmcnt<2 * LI * (NS - 2)>();      // this wave's part of block j has landed
+        __syncthreads();                      // ... everyone's, and stage (j-1) % NS is free
+        issue(j + NS - 1);
+        step(&ring[j % NS][0][0], j * BK, std::false_type{});
     }
     for (; j < nblk; ++j) {
-        const int buf = j & 1;
-        if (j + 1 < nblk) fetch(j + 1);
-        const int kb = j * BK;
-        if (!CAUSAL || kb <= wq_last + off) step(buf, kb, std::true_type{});
-        if (j + 1 < nblk) stage(buf ^ 1);
+        wait_vmcnt<2 * LI * (NS - 2)>();
         __syncthreads();
+        issue(j + NS - 1);
+        const int kb = j * BK;
+        if (!CAUSAL || kb <= wq_last + off) step(&ring[j % NS][0][0], kb, std::true_type{});
     }
+    wait_vmcnt<0>();    // no DMA may still be writing LDS when the workgroup retires
 
     // ---- epilogue: divide once, write O (bf16) and LSE (fp32) ----
     const float lsum = half_swap_sum(l);
@@ -287,14 +292,14 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __r
     }
 }
 
-template <int WAVES, bool CAUSAL>
+template <int WAVES, int NS, bool CAUSAL>
 hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
     constexpr int BQ = WAVES * 32;
     const int nqt = (a.Tq + BQ - 1) / BQ;
     const long long grid = (long long)nqt * a.B * a.H;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((prefill_bf16_d64_kernel<WAVES, CAUSAL>), dim3((unsigned)grid), dim3(WAVES * 64), 0, stream,
-                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+    hipLaunchKernelGGL((prefill_bf16_d64_kernel<WAVES, NS, CAUSAL>), dim3((unsigned)grid), dim3(WAVES * 64), 0,
+                       stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, a.Tq, a.Tkv,
                        a.B * a.H, nqt, a.c);
     return hipGetLastError();
@@ -309,11 +314,11 @@ bool prefill_bf16_fits(int Tkv) {
 
 hipError_t launch_prefill_bf16_d64(const PrefillArgs& a, hipStream_t stream, const char** name) {
     if (a.causal) {
-        *name = "prefill_bf16_d64<waves=4,bq=128,bk=64,causal>";
-        return launch_one<4, true>(a, stream);
+        *name = "prefill_bf16_d64<waves=4,bq=128,bk=64,stages=3,causal>";
+        return launch_one<4, 3, true>(a, stream);
     }
-    *name = "prefill_bf16_d64<waves=4,bq=128,bk=64>";
-    return launch_one<4, false>(a, stream);
+    *name = "prefill_bf16_d64<waves=4,bq=128,bk=64,stages=3>";
+    return launch_one<4, 3, false>(a, stream);
 }
 
 }  // namespace attn
