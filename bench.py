@@ -215,6 +215,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle leg: seconds of CPU work")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run 3 device-to-device copies of 512 MiB (a reference for HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -297,6 +299,13 @@ def main():
         result["decode"] = run_decode(torch, attn, args.steps, args.warmup)
         log(f"[bench] decode {result['decode']['kernel']}: {result['decode']['ms_per_step']:.3f} ms/step, "
             f"{result['decode']['value']:.0f} GB/s")
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = src.numel()
     print(json.dumps(result), flush=True)
 
 

@@ -71,6 +71,12 @@ __device__ __forceinline__ void buffer_load_lds_b128(__amdgpu_buffer_rsrc_t r, u
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 16, (int)voff, 0, 0, 0);
 }
 
+// Workgroup barrier without a memory fence.  __syncthreads() also waits for
+// every outstanding vector-memory operation, which would drain the LDS DMA
+// prefetch ring; callers that only need LDS data published wait for the DMA
+// they depend on with wait_vmcnt and have no LDS reads in flight.
+__device__ __forceinline__ void barrier_nofence() { __builtin_amdgcn_s_barrier(); }
+
 // s_waitcnt vmcnt(N) (other counters untouched); gfx9 encoding of the immediate.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -98,6 +104,19 @@ __device__ __forceinline__ u32x2_t lds_read_tr16_b64(uint32_t addr) {
 // reads them can be scheduled before the wait.
 __device__ __forceinline__ void lgkm_wait_4(u32x2_t& a, u32x2_t& b, u32x2_t& c, u32x2_t& d) {
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+
+// ds_read_b128 as inline asm, for the same reason as the transposed read.
+template <int OFF>
+__device__ __forceinline__ u32x4_t lds_read_b128(uint32_t addr) {
+    u32x4_t v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+// s_waitcnt lgkmcnt(N) with four 16-byte results flowing through it.
+template <int N>
+__device__ __forceinline__ void lgkm_wait_b128x4(u32x4_t& a, u32x4_t& b, u32x4_t& c, u32x4_t& d) {
+    asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "i"(N));
 }
 
 // DPP row-local exchanges: lanes are paired within rows of 16.
