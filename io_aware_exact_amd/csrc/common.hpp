@@ -106,12 +106,24 @@ __device__ __forceinline__ void lgkm_wait_4(u32x2_t& a, u32x2_t& b, u32x2_t& c, 
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
 }
 
+// s_waitcnt lgkmcnt(0) + vmcnt(N) (LDS traffic drained, LDS DMA up to N pending).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N & 0x30) << 10) | (0x7 << 4));
+}
+
 // ds_read_b128 as inline asm, for the same reason as the transposed read.
 template <int OFF>
 __device__ __forceinline__ u32x4_t lds_read_b128(uint32_t addr) {
     u32x4_t v;
     asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
     return v;
+}
+// s_waitcnt lgkmcnt(0) with eight 16-byte results flowing through it.
+__device__ __forceinline__ void lgkm_wait_b128x8(u32x4_t* a) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]));
 }
 // s_waitcnt lgkmcnt(N) with four 16-byte results flowing through it.
 template <int N>
