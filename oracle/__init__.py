@@ -29,6 +29,7 @@ and a library routine; none is "parity unpinned".
 
 from .attention import (
     attention,
+    attention_gqa,
     combine_partials,
     online_attention,
     online_softmax_states,
@@ -49,6 +50,7 @@ from .cost import (
 
 __all__ = [
     "attention",
+    "attention_gqa",
     "combine_partials",
     "online_attention",
     "online_softmax_states",

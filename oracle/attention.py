@@ -91,6 +91,34 @@ def attention(q, k, v, scale: float, causal: bool = False, rows=None):
     return o_out.reshape(lead + (row_idx.size, dv)), lse_out.reshape(lead + (row_idx.size,))
 
 
+def attention_gqa(q, k, v, scale: float, causal: bool = False, rows=None):
+    """Grouped-query attention: q is (B, H_q, T_q, d), k and v are
+    (B, H_kv, T_kv, d) with H_q a multiple of H_kv; query head h attends key /
+    value head h // (H_q / H_kv).
+
+    "Attention and Its Computational Cost", "The other shape: one query, many
+    keys": grouped-query attention keeps fewer key and value heads than query
+    heads, cutting the cache that every decode step reads.  Each query head is
+    the plain definition (``attention``) against its group's key/value head.
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be (B, H, T, d)")
+    B, hq = q.shape[0], q.shape[1]
+    hkv = k.shape[1]
+    if hkv < 1 or hq % hkv != 0 or v.shape[1] != hkv or k.shape[0] != B or v.shape[0] != B:
+        raise ValueError("H_q must be a multiple of H_kv")
+    group = hq // hkv
+    outs, lses = [], []
+    for h in range(hq):
+        o_h, l_h = attention(q[:, h], k[:, h // group], v[:, h // group], scale, causal, rows)
+        outs.append(o_h)
+        lses.append(l_h)
+    return np.stack(outs, axis=1), np.stack(lses, axis=1)
+
+
 def standard_attention(q, K, V):
     """One query against a full key set, score vector materialised.
 

@@ -444,3 +444,44 @@ def test_split_below_one_raises():
     rng = np.random.default_rng(26)
     with pytest.raises(ValueError):
         oracle.split_attention(_rand(rng, 1, 4), _rand(rng, 4, 4), _rand(rng, 4, 2), 0.5, 0)
+
+
+# ---------------------------------------------------------------- grouped-query heads
+
+def test_gqa_with_one_query_head_per_group_is_attention():
+    rng = np.random.default_rng(30)
+    q, k, v = _rand(rng, 2, 4, 3, 8), _rand(rng, 2, 4, 9, 8), _rand(rng, 2, 4, 9, 5)
+    for causal in (False, True):
+        o1, l1 = oracle.attention_gqa(q, k, v, 0.4, causal)
+        o2, l2 = attention(q, k, v, 0.4, causal)
+        np.testing.assert_array_equal(o1, o2)
+        np.testing.assert_array_equal(l1, l2)
+
+
+def test_gqa_equals_attention_on_repeated_heads():
+    """H_kv heads each shared by G query heads == full attention with every
+    key/value head repeated G times (consecutive query heads share one)."""
+    rng = np.random.default_rng(31)
+    B, hkv, G = 2, 3, 4
+    q = _rand(rng, B, hkv * G, 2, 8)
+    k, v = _rand(rng, B, hkv, 11, 8), _rand(rng, B, hkv, 11, 6)
+    o, lse = oracle.attention_gqa(q, k, v, 0.3)
+    kr, vr = np.repeat(k, G, axis=1), np.repeat(v, G, axis=1)
+    ob, lb = _brute(q[1, 7], kr[1, 7], vr[1, 7], 0.3, False)
+    np.testing.assert_allclose(o[1, 7], ob, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse[1, 7], lb, rtol=1e-13)
+    o2, l2 = attention(q, kr, vr, 0.3)
+    np.testing.assert_allclose(o, o2, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(lse, l2, rtol=1e-14)
+    # query head 5 belongs to group 1 (heads 4..7): it must ignore kv heads 0 and 2
+    k_alt = k.copy()
+    k_alt[:, 0] += 5.0
+    k_alt[:, 2] -= 5.0
+    o3, _ = oracle.attention_gqa(q, k_alt, v, 0.3)
+    np.testing.assert_array_equal(o3[:, 5], o[:, 5])
+
+
+def test_gqa_rejects_uneven_groups():
+    rng = np.random.default_rng(32)
+    with pytest.raises(ValueError):
+        oracle.attention_gqa(_rand(rng, 1, 6, 1, 4), _rand(rng, 1, 4, 5, 4), _rand(rng, 1, 4, 5, 4), 0.5)
