@@ -9,7 +9,9 @@ causal prefill, B=4, H=12, T=1024, d=64, bf16): the prefill kernel runs every
 prefill step of the hot path (Q tile load, K/V streaming, both products, the
 online softmax, causal skipping, the epilogue).  The decode half of the path
 (split-KV kernel + combine) is timed the same way on its own workload
-(B=64, H=32, T_kv=8192, d=128, 16 partitions) and reported in "decode".
+(B=64, H=32, T_kv=8192, d=128, 16 partitions) and reported in "decode", and
+its grouped-query form (the same step with 8 key/value heads for the 32 query
+heads) in "decode_gqa".
 
 Inputs are seeded synthetic tensors already resident in HBM when timing
 starts; W untimed warm-up steps are followed by exactly K timed steps,
@@ -59,7 +61,9 @@ def prefill_bytes(w) -> int:
 
 
 def decode_bytes(w) -> tuple[int, int]:
-    kv = 2 * w.B * w.H * w.Tkv * w.d * 2
+    """(all bytes, K/V-cache bytes) one decode step must move: K and V once
+    (kv_heads of them), q in, O and LSE out."""
+    kv = 2 * w.B * w.kv_heads * w.Tkv * w.d * 2
     return kv + 2 * w.B * w.H * w.d * 2 + w.B * w.H * 4, kv
 
 
@@ -151,18 +155,19 @@ def cpu_baseline_prefill(w, q, k, v, o_gpu, lse_gpu, min_seconds: float):
     }, {"max_abs_err_o": err_o, "max_abs_err_lse": err_l, "heads_checked": min(done, len(heads))}
 
 
-def run_decode(torch, attn, steps, warmup):
+def run_decode(torch, attn, steps, warmup, name="decode"):
     import numpy as np
 
     import oracle
     from io_aware_exact_amd.inputs import WORKLOADS, make_qkv, to_f64
 
-    w = WORKLOADS["decode"]
-    log(f"[bench] decode workload {w}: generating inputs")
+    w = WORKLOADS[name]
+    G = w.H // w.kv_heads
+    log(f"[bench] {name} workload {w}: generating inputs")
     t0 = time.perf_counter()
     q, k, v = make_qkv(w)
     dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
-    log(f"[bench] decode inputs ready in {time.perf_counter() - t0:.1f}s")
+    log(f"[bench] {name} inputs ready in {time.perf_counter() - t0:.1f}s")
     o = torch.empty_like(dq)
     lse = torch.empty((w.B, w.H), dtype=torch.float32, device="cuda")
     ws = torch.empty(attn.attn_decode_workspace_bytes(w.B, w.H, w.d, w.num_splits), dtype=torch.uint8, device="cuda")
@@ -175,21 +180,22 @@ def run_decode(torch, attn, steps, warmup):
     rng = np.random.default_rng(5)
     errs_o, errs_l = [], []
     for b, h in [(0, 0), (w.B - 1, w.H - 1)] + list(zip(rng.integers(0, w.B, 6).tolist(), rng.integers(0, w.H, 6).tolist())):
-        o_ref, lse_ref = oracle.attention(to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]), w.scale)
+        o_ref, lse_ref = oracle.attention(to_f64(q[b, h]), to_f64(k[b, h // G]), to_f64(v[b, h // G]), w.scale)
         errs_o.append(float(np.abs(to_f64(o[b, h]) - o_ref).max()))
         errs_l.append(float(abs(float(lse[b, h]) - lse_ref[0])))
-    # oracle leg, bounded: a few heads on the host
+    # oracle leg, bounded: a few query heads on the host
     sample_heads = 32
     t0 = time.perf_counter()
     for i in range(sample_heads):
         b, h = i % w.B, (7 * i) % w.H
-        oracle.attention(to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]), w.scale)
+        oracle.attention(to_f64(q[b, h]), to_f64(k[b, h // G]), to_f64(v[b, h // G]), w.scale)
     t_cpu = time.perf_counter() - t0
     cpu_gbps = sample_heads * (total / (w.B * w.H)) / t_cpu / 1e9
     del dq, dk, dv, q, k, v
     torch.cuda.empty_cache()
+    heads = f"H={w.H}" if G == 1 else f"Hq={w.H} Hkv={w.kv_heads}"
     return {
-        "workload": f"decode B={w.B} H={w.H} Tq=1 Tkv={w.Tkv} d={w.d} bf16 splits={w.num_splits}",
+        "workload": f"{name} B={w.B} {heads} Tq=1 Tkv={w.Tkv} d={w.d} bf16 splits={w.num_splits}",
         "metric": "decode attention KV-cache read bandwidth",
         "value": gbps,
         "unit": "GB/s",
@@ -199,10 +205,10 @@ def run_decode(torch, attn, steps, warmup):
         "warmup": warmup,
         "kernel": kern,
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": gbps / PEAK_HBM_GBPS, "traffic": measured_traffic("decode", "decode")},
+                     "frac": gbps / PEAK_HBM_GBPS, "traffic": measured_traffic("decode", name)},
         "parity": {"max_abs_err_o": max(errs_o), "max_abs_err_lse": max(errs_l), "heads_checked": len(errs_o)},
         "cpu_baseline": {"value": cpu_gbps, "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
-                         "sample": f"{sample_heads} (batch, head) slices, float64 numpy definition"},
+                         "sample": f"{sample_heads} (batch, query head) slices, float64 numpy definition"},
     }
 
 
@@ -296,9 +302,10 @@ def main():
     del dq, dk, dv
     torch.cuda.empty_cache()
     if not args.no_decode:
-        result["decode"] = run_decode(torch, attn, args.steps, args.warmup)
-        log(f"[bench] decode {result['decode']['kernel']}: {result['decode']['ms_per_step']:.3f} ms/step, "
-            f"{result['decode']['value']:.0f} GB/s")
+        for name in ("decode", "decode_gqa"):
+            result[name] = run_decode(torch, attn, args.steps, args.warmup, name)
+            log(f"[bench] {name} {result[name]['kernel']}: {result[name]['ms_per_step']:.3f} ms/step, "
+                f"{result[name]['value']:.0f} GB/s")
     if args.copy_calibration:
         src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)

@@ -110,6 +110,26 @@ int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * attn_decode_gqa -- attn_decode with grouped-query attention: Hq query heads
+ * share Hkv key/value heads, query head h reading key/value head
+ * h / (Hq / Hkv) ("Attention and Its Computational Cost", section "The other
+ * shape: one query, many keys": keeping fewer key and value heads than query
+ * heads shrinks the cache that every decode step streams).  Each K/V byte is
+ * read from memory once for all the query heads of its group.
+ *
+ *   q, o       bf16 [B,Hq,1,d];  k, v bf16 [B,Hkv,Tkv,d];  lse fp32 [B,Hq] or NULL
+ *   Hkv        >= 1 and dividing Hq (Hkv == Hq is attn_decode; Hkv == 1 is
+ *              multi-query attention)
+ *   workspace  at least attn_decode_workspace_bytes(B,Hq,d,num_splits) bytes
+ *   other arguments as attn_decode.
+ *
+ * Errors: ATTN_EINVAL also when Hkv < 1 or Hq % Hkv != 0.  Supported: d in {64, 128}.
+ */
+int attn_decode_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int Hq, int Hkv, int Tkv, int d, float scale, int num_splits,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * attn_last_kernel -- name and tile configuration of the kernel(s) enqueued by
  * this thread's last successful call, e.g.
  * "prefill_bf16_d64<waves=4,bq=128,bk=64,causal>" ("Attention and Its

@@ -12,6 +12,7 @@ from .attn import (
     ATTN_OK,
     AttnError,
     attn_decode,
+    attn_decode_gqa,
     attn_decode_workspace_bytes,
     attn_fwd,
     attn_fwd_f32,
@@ -24,6 +25,6 @@ from .attn import (
 
 __all__ = [
     "ATTN_EHIP", "ATTN_EINVAL", "ATTN_EUNSUPPORTED", "ATTN_EWORKSPACE", "ATTN_OK", "AttnError",
-    "attn_decode", "attn_decode_workspace_bytes", "attn_fwd", "attn_fwd_f32", "attn_last_kernel",
+    "attn_decode", "attn_decode_gqa", "attn_decode_workspace_bytes", "attn_fwd", "attn_fwd_f32", "attn_last_kernel",
     "attn_status_string", "lib", "prepared_decode", "prepared_fwd",
 ]

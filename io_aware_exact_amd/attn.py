@@ -31,6 +31,7 @@ SIGNATURES = {
     "attn_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
     "attn_decode_workspace_bytes": (_S, [_I, _I, _I, _I]),
     "attn_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _S, _P]),
+    "attn_decode_gqa": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _S, _P]),
     "attn_last_kernel": (ctypes.c_char_p, []),
     "attn_status_string": (ctypes.c_char_p, [_I]),
 }
@@ -131,29 +132,65 @@ def attn_decode_workspace_bytes(B: int, H: int, d: int, num_splits: int) -> int:
     return int(lib().attn_decode_workspace_bytes(B, H, d, num_splits))
 
 
+def _shape_gqa(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, T, d]")
+    B, Hq, Tq, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape[0] != B or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if Tq != 1:
+        raise ValueError("decode takes exactly one query per (batch, head)")
+    return B, Hq, Hkv, k.shape[2], d
+
+
+def _workspace(workspace, need: int, device):
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if workspace is None:
+        return None, 0
+    return _dev(workspace, "workspace", workspace.dtype), workspace.numel() * workspace.element_size()
+
+
 def attn_decode(q, k, v, scale: float | None = None, num_splits: int = 16, workspace=None, out=None, lse=None,
                 return_lse: bool = True):
     """One query per (batch, head): q [B,H,1,d], k/v [B,H,Tkv,d] -> (o, lse [B,H]).
 
     ``workspace`` (a uint8 GPU tensor) is allocated when not given.
     """
-    B, H, Tq, Tkv, d = _shape4(q, k, v)
-    if Tq != 1:
-        raise ValueError("attn_decode takes exactly one query per (batch, head)")
+    B, H, Hkv, Tkv, d = _shape_gqa(q, k, v)
+    if Hkv != H:
+        raise ValueError(f"attn_decode needs as many key/value heads as query heads ({Hkv} != {H}); "
+                         "use attn_decode_gqa")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else out
     if return_lse and lse is None:
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
     lp = _dev(lse, "lse", torch.float32) if return_lse else None
     splits = max(1, min(int(num_splits), Tkv))
-    need = attn_decode_workspace_bytes(B, H, d, splits)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    wp, wbytes = (None, 0) if workspace is None else (_dev(workspace, "workspace", workspace.dtype),
-                                                      workspace.numel() * workspace.element_size())
+    wp, wbytes = _workspace(workspace, attn_decode_workspace_bytes(B, H, d, splits), q.device)
     st = lib().attn_decode(_dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16), _dev(v, "v", torch.bfloat16),
                            _dev(o, "o", torch.bfloat16), lp, B, H, Tkv, d, scale, int(num_splits), wp, wbytes,
                            _stream())
+    _check(st)
+    return (o, lse) if return_lse else o
+
+
+def attn_decode_gqa(q, k, v, scale: float | None = None, num_splits: int = 16, workspace=None, out=None,
+                    lse=None, return_lse: bool = True):
+    """Grouped-query decode: q [B,Hq,1,d], k/v [B,Hkv,Tkv,d] with Hq % Hkv == 0
+    -> (o [B,Hq,1,d], lse [B,Hq]); query head h reads key/value head h // (Hq/Hkv)."""
+    B, Hq, Hkv, Tkv, d = _shape_gqa(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    lp = _dev(lse, "lse", torch.float32) if return_lse else None
+    splits = max(1, min(int(num_splits), Tkv))
+    wp, wbytes = _workspace(workspace, attn_decode_workspace_bytes(B, Hq, d, splits), q.device)
+    st = lib().attn_decode_gqa(_dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16),
+                               _dev(v, "v", torch.bfloat16), _dev(o, "o", torch.bfloat16), lp, B, Hq, Hkv, Tkv, d,
+                               scale, int(num_splits), wp, wbytes, _stream())
     _check(st)
     return (o, lse) if return_lse else o
 
@@ -186,15 +223,20 @@ def prepared_fwd(q, k, v, o, lse, causal: bool, scale: float | None = None, f32:
 
 
 def prepared_decode(q, k, v, o, lse, num_splits: int, workspace, scale: float | None = None):
-    """Zero-argument callable enqueuing attn_decode; see prepared_fwd."""
-    B, H, Tq, Tkv, d = _shape4(q, k, v)
+    """Zero-argument callable enqueuing attn_decode (or attn_decode_gqa when k
+    and v have fewer heads than q); see prepared_fwd."""
+    B, Hq, Hkv, Tkv, d = _shape_gqa(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     ptrs = [_dev(t, n, torch.bfloat16) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"))]
     lp = None if lse is None else _dev(lse, "lse", torch.float32)
     wp, wb = (None, 0) if workspace is None else (_dev(workspace, "workspace", workspace.dtype),
                                                   workspace.numel() * workspace.element_size())
-    fn = lib().attn_decode
-    args = (*ptrs, lp, B, H, Tkv, d, scale, int(num_splits), wp, wb, _stream())
+    if Hkv == Hq:
+        fn = lib().attn_decode
+        args = (*ptrs, lp, B, Hq, Tkv, d, scale, int(num_splits), wp, wb, _stream())
+    else:
+        fn = lib().attn_decode_gqa
+        args = (*ptrs, lp, B, Hq, Hkv, Tkv, d, scale, int(num_splits), wp, wb, _stream())
 
     def call():
         _check(fn(*args))

@@ -46,14 +46,17 @@ struct Range {
 bool overlap(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
 
 // Checks shared by every entry point.  `es` is the element size of q/k/v/o.
+// Q/O have H query heads, K/V have Hkv key/value heads.
 int check_common(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H,
-                 int Tq, int Tkv, int d, int causal, float scale, size_t es) {
+                 int Hkv, int Tq, int Tkv, int d, int causal, float scale, size_t es) {
     if (!q) return fail(ATTN_EINVAL, "q is NULL");
     if (!k) return fail(ATTN_EINVAL, "k is NULL");
     if (!v) return fail(ATTN_EINVAL, "v is NULL");
     if (!o) return fail(ATTN_EINVAL, "o is NULL");
     if (B < 1) return fail(ATTN_EINVAL, "B must be >= 1");
     if (H < 1) return fail(ATTN_EINVAL, "H must be >= 1");
+    if (Hkv < 1) return fail(ATTN_EINVAL, "Hkv must be >= 1");
+    if (H % Hkv != 0) return fail(ATTN_EINVAL, "the number of query heads must be a multiple of Hkv");
     if (Tq < 1) return fail(ATTN_EINVAL, "Tq must be >= 1");
     if (Tkv < 1) return fail(ATTN_EINVAL, "Tkv must be >= 1");
     if (d < 1) return fail(ATTN_EINVAL, "d must be >= 1");
@@ -65,7 +68,7 @@ int check_common(const void* q, const void* k, const void* v, const void* o, con
     if (lse && !aligned(lse, 4)) return fail(ATTN_EINVAL, "lse must be 4-byte aligned");
     // sizes: B*H*T*d*es must fit comfortably in 63 bits
     const double qbytes = double(B) * H * Tq * d * es;
-    const double kbytes = double(B) * H * Tkv * d * es;
+    const double kbytes = double(B) * Hkv * Tkv * d * es;
     if (qbytes > 4.0e18 || kbytes > 4.0e18) return fail(ATTN_EINVAL, "tensor sizes overflow");
     const uint64_t BH = uint64_t(B) * uint64_t(H);
     if (BH > 0x7fffffffull) return fail(ATTN_EINVAL, "B*H must fit in 31 bits");
@@ -90,9 +93,9 @@ int finish(hipError_t e, const char* name) {
     return ATTN_OK;
 }
 
-int run_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Tkv, int d,
-               float scale, int splits, void* ws, hipStream_t stream) {
-    attn::DecodeArgs a{q, k, v, o, lse, B, H, Tkv, d, splits, float(double(scale) * kLog2e), ws};
+int run_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int Tkv,
+               int d, float scale, int splits, void* ws, hipStream_t stream) {
+    attn::DecodeArgs a{q, k, v, o, lse, B, H, Hkv, Tkv, d, splits, float(double(scale) * kLog2e), ws};
     const char* name = nullptr;
     (void)hipGetLastError();   // clear any stale error so the launch status is ours
     return finish(attn::launch_decode_bf16(a, stream, &name), name);
@@ -104,13 +107,13 @@ extern "C" {
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Tq, int Tkv,
              int d, int causal, float scale, hipStream_t stream) {
-    int st = check_common(q, k, v, o, lse, B, H, Tq, Tkv, d, causal, scale, 2);
+    int st = check_common(q, k, v, o, lse, B, H, H, Tq, Tkv, d, causal, scale, 2);
     if (st != ATTN_OK) return st;
     if (Tq == 1) {
         // a single query row: the decode kernel, unsplit (bottom-right causal
         // alignment lets the one row see every key, so causal changes nothing)
         if (d != 64 && d != 128) return fail(ATTN_EUNSUPPORTED, "bf16 single-query path supports d in {64, 128}");
-        return run_decode(q, k, v, o, lse, B, H, Tkv, d, scale, 1, nullptr, stream);
+        return run_decode(q, k, v, o, lse, B, H, H, Tkv, d, scale, 1, nullptr, stream);
     }
     if (d != 64) return fail(ATTN_EUNSUPPORTED, "bf16 prefill supports d = 64");
     if (!attn::prefill_bf16_fits(Tkv)) return fail(ATTN_EUNSUPPORTED, "bf16 prefill supports Tkv*d*2 < 2^31 bytes per head");
@@ -123,7 +126,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
 
 int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int Tq,
                  int Tkv, int d, int causal, float scale, hipStream_t stream) {
-    int st = check_common(q, k, v, o, lse, B, H, Tq, Tkv, d, causal, scale, 4);
+    int st = check_common(q, k, v, o, lse, B, H, H, Tq, Tkv, d, causal, scale, 4);
     if (st != ATTN_OK) return st;
     if (!attn::prefill_f32_supports(d)) return fail(ATTN_EUNSUPPORTED, "fp32 path supports d in {16, 32, 64, 128}");
     if (double(B) * H * Tq > 2147483647.0) return fail(ATTN_EINVAL, "grid too large");
@@ -138,34 +141,40 @@ size_t attn_decode_workspace_bytes(int B, int H, int d, int num_splits) {
     return size_t(B) * size_t(H) * size_t(num_splits) * size_t(d + 2) * sizeof(float);
 }
 
-int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Tkv, int d,
-                float scale, int num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    int st = check_common(q, k, v, o, lse, B, H, 1, Tkv, d, 0, scale, 2);
+int attn_decode_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                    int Tkv, int d, float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+    int st = check_common(q, k, v, o, lse, B, Hq, Hkv, 1, Tkv, d, 0, scale, 2);
     if (st != ATTN_OK) return st;
     if (num_splits < 1) return fail(ATTN_EINVAL, "num_splits must be >= 1");
     if (d != 64 && d != 128) return fail(ATTN_EUNSUPPORTED, "decode supports d in {64, 128}");
     const int splits = num_splits > Tkv ? Tkv : num_splits;
     if (splits > 65535) return fail(ATTN_EUNSUPPORTED, "decode supports at most 65535 partitions");
     if (splits > 1) {
-        const size_t need = attn_decode_workspace_bytes(B, H, d, splits);
+        const size_t need = attn_decode_workspace_bytes(B, Hq, d, splits);
         if (!workspace) return fail(ATTN_EWORKSPACE, "workspace is NULL");
         if (workspace_bytes < need)
             return fail(ATTN_EWORKSPACE, "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " +
                                              std::to_string(need));
         if (!aligned(workspace, 16)) return fail(ATTN_EINVAL, "workspace must be 16-byte aligned");
         const uintptr_t w0 = reinterpret_cast<uintptr_t>(workspace), w1 = w0 + need;
-        const uint64_t kvb = uint64_t(B) * H * Tkv * d * 2, qb = uint64_t(B) * H * d * 2;
+        const uint64_t kvb = uint64_t(B) * Hkv * Tkv * d * 2, qb = uint64_t(B) * Hq * d * 2;
         const uintptr_t ptrs[4] = {reinterpret_cast<uintptr_t>(q), reinterpret_cast<uintptr_t>(k),
                                    reinterpret_cast<uintptr_t>(v), reinterpret_cast<uintptr_t>(o)};
         const uint64_t lens[4] = {qb, kvb, kvb, qb};
         for (int i = 0; i < 4; ++i)
             if (w0 < ptrs[i] + lens[i] && ptrs[i] < w1) return fail(ATTN_EINVAL, "workspace overlaps a tensor");
         if (lse) {
-            const uintptr_t l0 = reinterpret_cast<uintptr_t>(lse), l1 = l0 + uint64_t(B) * H * 4;
+            const uintptr_t l0 = reinterpret_cast<uintptr_t>(lse), l1 = l0 + uint64_t(B) * Hq * 4;
             if (w0 < l1 && l0 < w1) return fail(ATTN_EINVAL, "workspace overlaps lse");
         }
     }
-    return run_decode(q, k, v, o, lse, B, H, Tkv, d, scale, splits, workspace, stream);
+    return run_decode(q, k, v, o, lse, B, Hq, Hkv, Tkv, d, scale, splits, workspace, stream);
+}
+
+int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Tkv, int d,
+                float scale, int num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return attn_decode_gqa(q, k, v, o, lse, B, H, H, Tkv, d, scale, num_splits, workspace, workspace_bytes, stream);
 }
 
 const char* attn_last_kernel(void) { return g_last_kernel.c_str(); }

@@ -1,5 +1,5 @@
-// Exact attention for one query per (batch, head) against cached keys/values
-// (decode), bf16 inputs, head width 64 or 128, gfx950.
+// Exact attention for one query per (batch, query head) against cached keys
+// and values (decode), bf16 inputs, head width 64 or 128, gfx950.
 //
 // With a single query row there is nothing to tile in the query dimension and
 // the work is a streaming reduction over the cache, bound by reading K and V
@@ -11,51 +11,58 @@
 // partitions with the same rescaling ("IO-Aware Attention", section
 // "Parallelism and the cost of the split").
 //
-// Split kernel, one workgroup per (batch*head, partition):
-// * D/8 lanes share one key row: each lane holds 8 elements (16 bytes) of q
-//   and of the key, so a wave load instruction reads whole contiguous key rows
-//   (non-temporal: every byte is used once).
+// Grouped-query attention ("Attention and Its Computational Cost", same
+// section: fewer key/value heads than query heads shrink the cache): query
+// head h reads key/value head h / G with G = H_q / H_kv.  A workgroup serves
+// GT query heads of one group, so every K/V byte it loads is used by GT
+// queries; G = 1 is ordinary multi-head decode.
+//
+// Split kernel, one workgroup per (batch, kv head, head tile, partition):
+// * D/8 lanes share one key row: each lane holds 8 elements (16 bytes) of
+//   each of its GT queries and of the key, so a wave load instruction reads
+//   whole contiguous key rows (non-temporal: every byte is used once).
 // * q.k: v_dot2_f32_bf16 on the packed bf16 pairs, then a DPP sum over the
 //   D/8 lanes of the row.
 // * Each group of D/8 lanes keeps its own running (m, l) and 8-wide output
-//   slice, so the key loop has no cross-group traffic at all; groups and waves
-//   are merged once at the end through LDS.
+//   slice per query head, so the key loop has no cross-group traffic at all;
+//   groups and waves are merged once at the end through LDS.
 // * No LDS staging for K/V: nothing is reused, so loads go straight to VGPRs.
 //
-// Partial record per (batch*head, partition): o (D floats, not normalised),
-// then m (max of scale*log2e*q.k) and l, all fp32.
+// Partial record per (batch*query head, partition): o (D floats, not
+// normalised), then m (max of scale*log2e*q.k) and l, all fp32.
+#include <cstdio>
+
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace attn {
 namespace {
 
-constexpr int NW = 4;        // waves per workgroup
-constexpr int UNROLL = 8;    // key-row loads in flight per lane per operand
+constexpr int NW = 4;   // waves per workgroup
 
-template <int D>
+template <int D, int GT>
 struct DecodeShape {
     static constexpr int LPK = D / 8;          // lanes per key row
     static constexpr int KPW = 64 / LPK;       // key rows per wave load
-    static constexpr int GROUPS = NW * KPW;    // independent softmax states per workgroup
+    static constexpr int GROUPS = NW * KPW;    // independent softmax states per workgroup and head
+    static constexpr int UNROLL = GT >= 4 ? 4 : 8;   // key-row loads in flight per lane per operand
     static constexpr int STEP = NW * KPW * UNROLL;   // keys per workgroup iteration
+    static constexpr int HP = GT < 4 ? GT : 4;       // heads merged per LDS pass
 };
 
-template <int LPK>
-__device__ __forceinline__ float row_sum(float v) { return group_sum<LPK>(v); }
-
-template <int D>
+template <int D, int GT>
 __global__ __launch_bounds__(NW * 64)
 void decode_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                          const uint16_t* __restrict__ V, float* __restrict__ part,
                          uint16_t* __restrict__ O, float* __restrict__ LSE,
-                         int Tkv, int P, float c, int direct) {
-    using S = DecodeShape<D>;
-    constexpr int LPK = S::LPK, KPW = S::KPW, GROUPS = S::GROUPS, STEP = S::STEP;
+                         int Hkv, int G, int Tkv, int P, float c, int direct) {
+    using S = DecodeShape<D, GT>;
+    constexpr int LPK = S::LPK, KPW = S::KPW, GROUPS = S::GROUPS, UNROLL = S::UNROLL, STEP = S::STEP;
+    constexpr int HP = S::HP;
 
-    __shared__ float red_o[GROUPS][D];
-    __shared__ float red_m[GROUPS];
-    __shared__ float red_l[GROUPS];
+    __shared__ float red_o[HP][GROUPS][D];
+    __shared__ float red_m[HP][GROUPS];
+    __shared__ float red_l[HP][GROUPS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -64,18 +71,32 @@ void decode_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     const int dc = lane % LPK;         // which 8 elements of the row
     const int grp = wave * KPW + kr;   // softmax-state group
 
-    const int bh = blockIdx.x;
+    // blockIdx.x = (b * Hkv + hk) * (G / GT) + tile
+    const int tiles = G / GT;
+    const int bkv = blockIdx.x / tiles;
+    const int tile = blockIdx.x - bkv * tiles;
+    const int b = bkv / Hkv;
+    const int hk = bkv - b * Hkv;
+    const int Hq = Hkv * G;
+    const int qh0 = b * Hq + hk * G + tile * GT;   // first (batch*query head) row of this tile
     const int p = blockIdx.y;
     const long long lo = ((long long)p * Tkv) / P;
     const long long hi = ((long long)(p + 1) * Tkv) / P;
 
-    const size_t kvbase = (size_t)bh * Tkv * D;
-    const u32x4_t qw = *reinterpret_cast<const u32x4_t*>(Q + (size_t)bh * D + 8 * dc);
-
-    float m = kNegInf, l = 0.f;
-    float o[8];
+    const size_t kvbase = (size_t)bkv * Tkv * D;
+    u32x4_t qw[GT];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = 0.f;
+    for (int t = 0; t < GT; ++t)
+        qw[t] = *reinterpret_cast<const u32x4_t*>(Q + (size_t)(qh0 + t) * D + 8 * dc);
+
+    float m[GT], l[GT], o[GT][8];
+#pragma unroll
+    for (int t = 0; t < GT; ++t) {
+        m[t] = kNegInf;
+        l[t] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[t][i] = 0.f;
+    }
 
     for (long long base = lo; base < hi; base += STEP) {
         u32x4_t kw[UNROLL], vw[UNROLL];
@@ -92,71 +113,96 @@ void decode_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
                 vw[u] = u32x4_t{0, 0, 0, 0};
             }
         }
-        float s[UNROLL];
-        float mx = kNegInf;
+        float s[UNROLL][GT];
+        float mx[GT];
+#pragma unroll
+        for (int t = 0; t < GT; ++t) mx[t] = kNegInf;
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
-            float acc = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kw[u][i]), as_bf16x2(qw[i]), acc, false);
-            acc = row_sum<LPK>(acc);
             const long long key = base + (long long)(wave * UNROLL + u) * KPW + kr;
-            s[u] = (key < hi) ? acc * c : kNegInf;
-            mx = fmaxf(mx, s[u]);
-        }
-        const float m_new = fmaxf(m, mx);
-        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-        const float alpha = fast_exp2(m - m_use);
-        l *= alpha;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] *= alpha;
+            for (int t = 0; t < GT; ++t) {
+                float acc = 0.f;
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const float pu = fast_exp2(s[u] - m_use);
-            l += pu;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                o[2 * i] = __builtin_fmaf(pu, bf16_lo(vw[u][i]), o[2 * i]);
-                o[2 * i + 1] = __builtin_fmaf(pu, bf16_hi(vw[u][i]), o[2 * i + 1]);
+                for (int i = 0; i < 4; ++i)
+                    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kw[u][i]), as_bf16x2(qw[t][i]), acc, false);
+                acc = group_sum<LPK>(acc);
+                s[u][t] = (key < hi) ? acc * c : kNegInf;
+                mx[t] = fmaxf(mx[t], s[u][t]);
             }
         }
-        m = m_new;
+        float m_use[GT];
+#pragma unroll
+        for (int t = 0; t < GT; ++t) {
+            const float m_new = fmaxf(m[t], mx[t]);
+            m_use[t] = (m_new == kNegInf) ? 0.f : m_new;
+            const float alpha = fast_exp2(m[t] - m_use[t]);
+            l[t] *= alpha;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[t][i] *= alpha;
+            m[t] = m_new;
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            float vf[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                vf[2 * i] = bf16_lo(vw[u][i]);
+                vf[2 * i + 1] = bf16_hi(vw[u][i]);
+            }
+#pragma unroll
+            for (int t = 0; t < GT; ++t) {
+                const float pu = fast_exp2(s[u][t] - m_use[t]);
+                l[t] += pu;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) o[t][i] = __builtin_fmaf(pu, vf[i], o[t][i]);
+            }
+        }
     }
 
-    // ---- merge the GROUPS states of this workgroup ----
+    // ---- merge the GROUPS states of this workgroup, HP heads per LDS pass ----
 #pragma unroll
-    for (int i = 0; i < 8; ++i) red_o[grp][8 * dc + i] = o[i];
-    if (dc == 0) {
-        red_m[grp] = m;
-        red_l[grp] = l;
-    }
-    __syncthreads();
-    for (int d = tid; d < D; d += NW * 64) {
-        float M = kNegInf;
-        for (int g = 0; g < GROUPS; ++g) M = fmaxf(M, red_m[g]);
-        const float Mu = (M == kNegInf) ? 0.f : M;
-        float L = 0.f, acc = 0.f;
-        for (int g = 0; g < GROUPS; ++g) {
-            const float w = fast_exp2(red_m[g] - Mu);
-            L += w * red_l[g];
-            acc += w * red_o[g][d];
+    for (int t0 = 0; t0 < GT; t0 += HP) {
+        if (t0 > 0) __syncthreads();   // the previous pass has finished reading
+#pragma unroll
+        for (int t = 0; t < HP; ++t) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) red_o[t][grp][8 * dc + i] = o[t0 + t][i];
+            if (dc == 0) {
+                red_m[t][grp] = m[t0 + t];
+                red_l[t][grp] = l[t0 + t];
+            }
         }
-        if (direct) {
-            O[(size_t)bh * D + d] = (uint16_t)(pack_bf16x2(acc / L, 0.f) & 0xffffu);
-            if (d == 0 && LSE != nullptr) LSE[bh] = (M + __builtin_log2f(L)) * 0.69314718055994530942f;
-        } else {
-            float* rec = part + ((size_t)bh * P + p) * (D + 2);
-            rec[d] = acc;
-            if (d == 0) {
-                rec[D] = M;
-                rec[D + 1] = L;
+        __syncthreads();
+        for (int e = tid; e < HP * D; e += NW * 64) {
+            const int t = e / D;
+            const int d = e - t * D;
+            float M = kNegInf;
+            for (int g = 0; g < GROUPS; ++g) M = fmaxf(M, red_m[t][g]);
+            const float Mu = (M == kNegInf) ? 0.f : M;
+            float L = 0.f, acc = 0.f;
+            for (int g = 0; g < GROUPS; ++g) {
+                const float w = fast_exp2(red_m[t][g] - Mu);
+                L += w * red_l[t][g];
+                acc += w * red_o[t][g][d];
+            }
+            const int row = qh0 + t0 + t;
+            if (direct) {
+                O[(size_t)row * D + d] = (uint16_t)(pack_bf16x2(acc / L, 0.f) & 0xffffu);
+                if (d == 0 && LSE != nullptr) LSE[row] = (M + __builtin_log2f(L)) * 0.69314718055994530942f;
+            } else {
+                float* rec = part + ((size_t)row * P + p) * (D + 2);
+                rec[d] = acc;
+                if (d == 0) {
+                    rec[D] = M;
+                    rec[D + 1] = L;
+                }
             }
         }
     }
 }
 
-// One workgroup of D threads per (batch, head): merge its P partial records.
+// One workgroup of D threads per (batch, query head): merge its P partial records.
 template <int D>
 __global__ __launch_bounds__(D)
 void decode_combine_kernel(const float* __restrict__ part, uint16_t* __restrict__ O,
@@ -178,23 +224,47 @@ void decode_combine_kernel(const float* __restrict__ part, uint16_t* __restrict_
     if (d == 0 && LSE != nullptr) LSE[bh] = (M + __builtin_log2f(L)) * 0.69314718055994530942f;
 }
 
-template <int D>
-hipError_t launch_d(const DecodeArgs& a, hipStream_t stream, const char** name) {
-    const int BH = a.B * a.H;
+// Largest head tile (8, 4, 2 or 1) that divides the group size.
+int head_tile(int G) {
+    for (int gt : {8, 4, 2})
+        if (G % gt == 0) return gt;
+    return 1;
+}
+
+thread_local char g_name[96];
+
+template <int D, int GT>
+hipError_t launch_dg(const DecodeArgs& a, hipStream_t stream, const char** name) {
+    const int G = a.H / a.Hkv;
+    const int blocks = a.B * a.Hkv * (G / GT);
     const bool direct = (a.num_splits == 1);
-    hipLaunchKernelGGL((decode_split_kernel<D>), dim3(BH, a.num_splits), dim3(NW * 64), 0, stream,
+    hipLaunchKernelGGL((decode_split_kernel<D, GT>), dim3(blocks, a.num_splits), dim3(NW * 64), 0, stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), static_cast<float*>(a.workspace),
-                       static_cast<uint16_t*>(a.o), a.lse, a.Tkv, a.num_splits, a.c, direct ? 1 : 0);
+                       static_cast<uint16_t*>(a.o), a.lse, a.Hkv, G, a.Tkv, a.num_splits, a.c, direct ? 1 : 0);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || direct) {
-        *name = (D == 128) ? "decode_bf16_d128<splits=1,waves=4>" : "decode_bf16_d64<splits=1,waves=4>";
-        return e;
+    if (e == hipSuccess && !direct) {
+        hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.H), dim3(D), 0, stream,
+                           static_cast<const float*>(a.workspace), static_cast<uint16_t*>(a.o), a.lse,
+                           a.num_splits);
+        e = hipGetLastError();
     }
-    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(BH), dim3(D), 0, stream,
-                       static_cast<const float*>(a.workspace), static_cast<uint16_t*>(a.o), a.lse, a.num_splits);
-    *name = (D == 128) ? "decode_split_bf16_d128<waves=4>+combine" : "decode_split_bf16_d64<waves=4>+combine";
-    return hipGetLastError();
+    if (direct)
+        snprintf(g_name, sizeof g_name, "decode_bf16_d%d<heads=%d,splits=1,waves=4>", D, GT);
+    else
+        snprintf(g_name, sizeof g_name, "decode_split_bf16_d%d<heads=%d,waves=4>+combine", D, GT);
+    *name = g_name;
+    return e;
+}
+
+template <int D>
+hipError_t launch_d(const DecodeArgs& a, hipStream_t stream, const char** name) {
+    switch (head_tile(a.H / a.Hkv)) {
+        case 8: return launch_dg<D, 8>(a, stream, name);
+        case 4: return launch_dg<D, 4>(a, stream, name);
+        case 2: return launch_dg<D, 2>(a, stream, name);
+        default: return launch_dg<D, 1>(a, stream, name);
+    }
 }
 
 }  // namespace

@@ -24,7 +24,7 @@ struct DecodeArgs {
     const void* v;
     void* o;
     float* lse;
-    int B, H, Tkv, d;
+    int B, H, Hkv, Tkv, d;   // H query heads, Hkv key/value heads (H % Hkv == 0)
     int num_splits;   // already clamped to [1, Tkv]
     float c;          // scale * log2(e)
     void* workspace;  // B*H*num_splits*(d+2) floats, unused when num_splits == 1

@@ -8,7 +8,8 @@ Recipe (the pages' workloads are random N(0,1) tensors at GPT-2's head shape
 and at the sizes listed in ``WORKLOADS``):
 
 * tensor ``t`` in (q=0, k=1, v=2), batch row ``b``: draw
-  ``numpy.random.default_rng([seed, t, b]).standard_normal((H, T, d), float32)``;
+  ``numpy.random.default_rng([seed, t, b]).standard_normal((H, T, d), float32)``
+  (H is the number of key/value heads for k and v);
 * multiply by the tensor's factor in float32 (K x 3 for the mid-length
   workload, 1 otherwise);
 * round to bfloat16 by round-to-nearest-even (torch's float32 -> bfloat16
@@ -46,10 +47,15 @@ class Workload:
     k_factor: float = 1.0
     num_splits: int = 1
     block: int = 64
+    Hkv: int | None = None   # key/value heads (grouped-query); None = H
 
     @property
     def scale(self) -> float:
         return 1.0 / math.sqrt(self.d)
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H if self.Hkv is None else self.Hkv
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -67,6 +73,9 @@ WORKLOADS = {
     "long": Workload("long", 1, 12, 16384, 16384, 64, "bf16", True, seed=4),
     # one query per sequence against 8,192 cached keys, split-KV into 16 chunks
     "decode": Workload("decode", 64, 32, 1, 8192, 128, "bf16", False, seed=5, num_splits=16),
+    # the same decode step with grouped-query attention: 32 query heads over
+    # 8 key/value heads (groups of 4), so a quarter of the cache
+    "decode_gqa": Workload("decode_gqa", 64, 32, 1, 8192, 128, "bf16", False, seed=6, num_splits=16, Hkv=8),
 }
 
 
@@ -117,8 +126,8 @@ def make_tensor(seed: int, tensor: str, B: int, H: int, T: int, d: int, dtype: s
 def make_qkv(w: Workload, batch_rows=None):
     """(q, k, v) CPU tensors for a workload (see the module recipe)."""
     q = make_tensor(w.seed, "q", w.B, w.H, w.Tq, w.d, w.dtype, 1.0, batch_rows)
-    k = make_tensor(w.seed, "k", w.B, w.H, w.Tkv, w.d, w.dtype, w.k_factor, batch_rows)
-    v = make_tensor(w.seed, "v", w.B, w.H, w.Tkv, w.d, w.dtype, 1.0, batch_rows)
+    k = make_tensor(w.seed, "k", w.B, w.kv_heads, w.Tkv, w.d, w.dtype, w.k_factor, batch_rows)
+    v = make_tensor(w.seed, "v", w.B, w.kv_heads, w.Tkv, w.d, w.dtype, 1.0, batch_rows)
     return q, k, v
 
 

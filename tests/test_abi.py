@@ -65,6 +65,14 @@ def dec(lib, **kw):
                            a["P"], a["ws"], a["wsb"], a["stream"])
 
 
+def gqa(lib, **kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, Hq=8, Hkv=2, Tkv=100, d=128, scale=0.088, P=4, ws=W, wsb=1 << 30,
+             stream=None)
+    a.update(kw)
+    return lib.attn_decode_gqa(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Tkv"],
+                               a["d"], a["scale"], a["P"], a["ws"], a["wsb"], a["stream"])
+
+
 @pytest.mark.parametrize("call", [fwd, fwd32])
 @pytest.mark.parametrize("bad, want", [
     (dict(q=None), "q is NULL"), (dict(k=None), "k is NULL"), (dict(v=None), "v is NULL"),
@@ -102,6 +110,23 @@ def test_decode_arguments(lib):
     assert dec(lib, q=None) == EINVAL
     assert dec(lib, scale=0.0) == EINVAL
     assert dec(lib, Tkv=0) == EINVAL
+
+
+def test_gqa_decode_arguments(lib):
+    assert gqa(lib, Hkv=0) == EINVAL and "Hkv" in attn.attn_status_string(EINVAL)
+    assert gqa(lib, Hkv=3) == EINVAL and "multiple of Hkv" in attn.attn_status_string(EINVAL)
+    assert gqa(lib, Hkv=16) == EINVAL
+    assert gqa(lib, Hq=0) == EINVAL
+    assert gqa(lib, d=96) == EUNSUP
+    assert gqa(lib, P=0) == EINVAL
+    assert gqa(lib, ws=None) == EWS
+    # the workspace is sized by query heads
+    need = attn.attn_decode_workspace_bytes(2, 8, 128, 4)
+    assert gqa(lib, wsb=need - 1) == EWS and str(need) in attn.attn_status_string(EWS)
+    # k/v extents use Hkv heads: B*Hkv*Tkv*d*2 bytes = 102400 bytes from K
+    kv_bytes = 2 * 2 * 100 * 128 * 2
+    assert gqa(lib, o=K + kv_bytes - 256) == EINVAL and "o overlaps k" in attn.attn_status_string(EINVAL)
+    assert gqa(lib, ws=K + kv_bytes - 64) == EINVAL and "overlaps" in attn.attn_status_string(EINVAL)
 
 
 def test_workspace_size_formula():

@@ -169,6 +169,61 @@ def test_decode_shapes(B, H, Tkv, d, splits):
     assert ("combine" in attn.attn_last_kernel()) == (min(splits, Tkv) > 1)
 
 
+def gqa_check(w: Workload):
+    say(f"case {w}")
+    q, k, v = make_qkv(w)
+    o, lse = attn.attn_decode_gqa(q.cuda(), k.cuda(), v.cuda(), scale=w.scale, num_splits=w.num_splits)
+    torch.cuda.synchronize()
+    kern = attn.attn_last_kernel()
+    say(f"  kernel {kern}")
+    o_ref, lse_ref = oracle.attention_gqa(to_f64(q), to_f64(k), to_f64(v), w.scale)
+    compare(w, o, lse[:, :, None], o_ref, lse_ref)
+    return kern
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Tkv,d,splits", [
+    (2, 8, 8, 700, 128, 4),      # one query head per group: attn_decode's case
+    (2, 8, 4, 700, 128, 4),      # groups of 2
+    (2, 8, 2, 1000, 128, 16),    # groups of 4
+    (2, 8, 1, 1000, 128, 7),     # multi-query: one key/value head
+    (1, 16, 2, 513, 128, 1),     # groups of 8, unsplit
+    (3, 6, 2, 301, 64, 5),       # groups of 3 (head tile 1)
+    (2, 12, 2, 257, 64, 3),      # groups of 6 (head tile 2)
+    (1, 32, 2, 90, 64, 200),     # groups of 16 (two tiles of 8), splits clamped to Tkv
+    (1, 4, 1, 1, 128, 16),       # a single cached key
+])
+def test_gqa_decode_shapes(B, Hq, Hkv, Tkv, d, splits):
+    kern = gqa_check(Workload(f"gqa[{B},{Hq}/{Hkv},{Tkv},d={d},P={splits}]", B, Hq, 1, Tkv, d, "bf16", False,
+                              seed=40 + Hq + Tkv, num_splits=splits, Hkv=Hkv))
+    assert ("combine" in kern) == (min(splits, Tkv) > 1)
+
+
+def test_gqa_decode_full_size_sampled():
+    w = WORKLOADS["decode_gqa"]
+    say(f"case {w} (sampled heads)")
+    q, k, v = make_qkv(w)
+    dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
+    o, lse = attn.attn_decode_gqa(dq, dk, dv, scale=w.scale, num_splits=w.num_splits)
+    torch.cuda.synchronize()
+    say(f"  kernel {attn.attn_last_kernel()}")
+    G = w.H // w.kv_heads
+    rng = np.random.default_rng(78)
+    picks = [(0, 0), (w.B - 1, w.H - 1)] + [(int(b), int(h)) for b, h in
+                                            zip(rng.integers(0, w.B, 14), rng.integers(0, w.H, 14))]
+    for b, h in picks:
+        o_ref, lse_ref = oracle.attention(to_f64(q[b, h]), to_f64(k[b, h // G]), to_f64(v[b, h // G]), w.scale)
+        compare(w, o[b, h], lse[b, h], o_ref, lse_ref, what=f"[b={b},h={h}]")
+    # against the multi-head kernel on key/value heads repeated G times
+    kr = dk.repeat_interleave(G, dim=1).contiguous()
+    vr = dv.repeat_interleave(G, dim=1).contiguous()
+    o1, lse1 = attn.attn_decode(dq, kr, vr, scale=w.scale, num_splits=w.num_splits)
+    torch.cuda.synchronize()
+    dO = float((o1.float() - o.float()).abs().max())
+    dL = float((lse1 - lse).abs().max())
+    say(f"  grouped vs repeated heads max|dO|={dO:.3e} max|dLSE|={dL:.3e}")
+    assert dO <= 2e-2 and dL <= TOL_LSE
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_single_query_through_attn_fwd(d):
     w = Workload(f"fwd_tq1[d={d}]", 3, 4, 1, 2049, d, "bf16", True, seed=21)
