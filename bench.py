@@ -11,7 +11,9 @@ online softmax, causal skipping, the epilogue).  The decode half of the path
 (split-KV kernel + combine) is timed the same way on its own workload
 (B=64, H=32, T_kv=8192, d=128, 16 partitions) and reported in "decode", and
 its grouped-query form (the same step with 8 key/value heads for the 32 query
-heads) in "decode_gqa".
+heads) in "decode_gqa".  "prefill_split" times one 16K-token causal head, a
+shape with too few query tiles to fill the chip, with and without the key
+axis split across workgroups.
 
 Inputs are seeded synthetic tensors already resident in HBM when timing
 starts; W untimed warm-up steps are followed by exactly K timed steps,
@@ -212,13 +214,55 @@ def run_decode(torch, attn, steps, warmup, name="decode"):
     }
 
 
+def run_prefill_split(torch, attn, steps, warmup, name="long_1head"):
+    """Prefill on a shape with too few query tiles to fill the chip: attn_fwd
+    (one workgroup per query tile) against attn_fwd_split (the key axis of
+    long tiles split across workgroups, then merged), same inputs."""
+    from io_aware_exact_amd.inputs import WORKLOADS, make_qkv
+
+    w = WORKLOADS[name]
+    q, k, v = make_qkv(w)
+    dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
+    o = torch.empty_like(dq)
+    lse = torch.empty((w.B, w.H, w.Tq), dtype=torch.float32, device="cuda")
+    ms_plain = time_steps(torch, attn.prepared_fwd(dq, dk, dv, o, lse, w.causal, w.scale), steps, warmup)
+    kern_plain = attn.attn_last_kernel()
+    o_plain = o.clone()
+    nbytes = attn.attn_fwd_split_workspace_bytes(w.B, w.H, w.Tq, w.Tkv, w.d, w.causal, 0)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    call = attn.prepared_fwd(dq, dk, dv, o, lse, w.causal, w.scale, kv_chunk=0, workspace=ws)
+    ms = time_steps(torch, call, steps, warmup)
+    kern = attn.attn_last_kernel()
+    diff = float((o.float() - o_plain.float()).abs().max())
+    flops = prefill_flops(w)
+    del dq, dk, dv, ws, o_plain
+    torch.cuda.empty_cache()
+    tf = flops / (ms * 1e-3) / 1e12
+    return {
+        "workload": f"{name} prefill B={w.B} H={w.H} Tq={w.Tq} Tkv={w.Tkv} d={w.d} "
+                    f"{'causal' if w.causal else 'non-causal'} bf16",
+        "metric": "attn fwd TFLOP/s (causal-adjusted), key axis split across workgroups",
+        "value": tf,
+        "unit": "TFLOP/s",
+        "ms_per_step": ms,
+        "kernel": kern,
+        "workspace_bytes": nbytes,
+        "unsplit": {"ms_per_step": ms_plain, "value": flops / (ms_plain * 1e-3) / 1e12, "kernel": kern_plain},
+        "speedup_vs_unsplit": ms_plain / ms,
+        "max_abs_diff_vs_unsplit_o": diff,
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / PEAK_BF16_TFLOPS, "traffic": None},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gpt2", help="prefill workload: gpt2, mid, mid_causal, long, tiny")
-    ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode measurements")
+    ap.add_argument("--no-split", action="store_true", help="skip the split-prefill measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle leg: seconds of CPU work")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -301,6 +345,11 @@ def main():
         result["cpu_baseline"] = None
     del dq, dk, dv
     torch.cuda.empty_cache()
+    if not args.no_split:
+        result["prefill_split"] = run_prefill_split(torch, attn, args.steps, args.warmup)
+        log(f"[bench] prefill_split {result['prefill_split']['kernel']}: "
+            f"{result['prefill_split']['ms_per_step'] * 1e3:.1f} us/step "
+            f"(unsplit {result['prefill_split']['unsplit']['ms_per_step'] * 1e3:.1f} us)")
     if not args.no_decode:
         for name in ("decode", "decode_gqa"):
             result[name] = run_decode(torch, attn, args.steps, args.warmup, name)

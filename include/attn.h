@@ -18,8 +18,9 @@
  * units of the scaled score, kept for a backward pass ("IO-Aware Attention",
  * section "What has to stay in fast memory").
  *
- * Layout: Q and O are [B, H, T_q, d], K and V are [B, H, T_kv, d], all
- * contiguous row-major with d innermost; LSE is [B, H, T_q] fp32.  bf16 data
+ * Layout: Q and O are [B, H, T_q, d], K and V are [B, H, T_kv, d] (H_kv key/value
+ * heads for attn_decode_gqa), all contiguous row-major with d innermost; LSE is
+ * [B, H, T_q] fp32.  bf16 data
  * is passed as 16-bit words (the upper half of the IEEE fp32 bit pattern).
  *
  * Ownership: every pointer is caller-owned device memory.  The library never
@@ -51,7 +52,7 @@ enum {
                                pointer not 16-byte aligned, num_splits < 1, aliasing output, sizes overflow */
     ATTN_EUNSUPPORTED = -2, /* head width d not built for this path */
     ATTN_EHIP = -3,         /* the HIP runtime reported an error while enqueueing */
-    ATTN_EWORKSPACE = -4    /* decode workspace missing or smaller than attn_decode_workspace_bytes() */
+    ATTN_EWORKSPACE = -4    /* workspace missing or smaller than the call's *_workspace_bytes() */
 };
 
 /*
@@ -72,6 +73,41 @@ enum {
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int Tq, int Tkv, int d, int causal, float scale, hipStream_t stream);
+
+/*
+ * attn_fwd_split_workspace_bytes -- bytes of workspace attn_fwd_split needs for
+ * this shape and kv_chunk; 0 when that call would not split (then it needs no
+ * workspace) or when the arguments are invalid.
+ */
+size_t attn_fwd_split_workspace_bytes(int B, int H, int Tq, int Tkv, int d, int causal, int kv_chunk);
+
+/*
+ * attn_fwd_split -- attn_fwd with the key axis of long query tiles split
+ * across workgroups ("IO-Aware Attention", section "Parallelism and the cost
+ * of the split": when the query blocks alone do not fill the device, key
+ * partitions each produce a partial output and normaliser, merged with the
+ * same rescaling).  The result equals attn_fwd's up to fp32 rounding order.
+ *
+ *   kv_chunk   keys per work unit, rounded up to a multiple of 64; a query tile
+ *              (128 rows) whose key range is longer is split into
+ *              ceil(range / kv_chunk) near-equal chunks.  0 = the library
+ *              picks: it splits only when there are fewer query tiles than
+ *              3 per compute unit (768), into chunks of an even share of all
+ *              key blocks over 768 units but at least 1024 keys, and only
+ *              tiles longer than that.
+ *   workspace  device memory of at least attn_fwd_split_workspace_bytes(...)
+ *              bytes (may be NULL when that is 0); contents on entry are
+ *              ignored.  Partials of split tiles: per (batch, head, tile,
+ *              chunk) 128 x d fp32 values and 128 fp32 log-sum-exps.
+ *   other arguments as attn_fwd.
+ *
+ * When split, a second kernel (the merge) follows on the same stream.
+ * Errors: as attn_fwd; ATTN_EINVAL for kv_chunk < 0; ATTN_EWORKSPACE when a
+ * split is planned and the workspace is NULL or too small.
+ */
+int attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Tq, int Tkv, int d, int causal, float scale, int kv_chunk,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * attn_fwd_f32 -- the exact path: fp32 inputs, fp32 products, fp32 output.

@@ -28,6 +28,8 @@ _F = ctypes.c_float
 _S = ctypes.c_size_t
 SIGNATURES = {
     "attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "attn_fwd_split_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I, _I]),
+    "attn_fwd_split": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _S, _P]),
     "attn_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
     "attn_decode_workspace_bytes": (_S, [_I, _I, _I, _I]),
     "attn_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _S, _P]),
@@ -109,6 +111,31 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None
     lp = _dev(lse, "lse", torch.float32) if return_lse else None
     st = lib().attn_fwd(_dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16), _dev(v, "v", torch.bfloat16),
                         _dev(o, "o", torch.bfloat16), lp, B, H, Tq, Tkv, d, int(bool(causal)), scale, _stream())
+    _check(st)
+    return (o, lse) if return_lse else o
+
+
+def attn_fwd_split_workspace_bytes(B: int, H: int, Tq: int, Tkv: int, d: int, causal: bool,
+                                   kv_chunk: int = 0) -> int:
+    return int(lib().attn_fwd_split_workspace_bytes(B, H, Tq, Tkv, d, int(bool(causal)), int(kv_chunk)))
+
+
+def attn_fwd_split(q, k, v, causal: bool = False, scale: float | None = None, kv_chunk: int = 0, workspace=None,
+                   out=None, lse=None, return_lse: bool = True):
+    """bf16 forward with long query tiles split over the key axis (see
+    include/attn.h); ``workspace`` (a GPU tensor) is allocated when needed and
+    not given."""
+    B, H, Tq, Tkv, d = _shape4(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, Tq), dtype=torch.float32, device=q.device)
+    lp = _dev(lse, "lse", torch.float32) if return_lse else None
+    wp, wbytes = _workspace(workspace, attn_fwd_split_workspace_bytes(B, H, Tq, Tkv, d, causal, kv_chunk),
+                            q.device)
+    st = lib().attn_fwd_split(_dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16),
+                              _dev(v, "v", torch.bfloat16), _dev(o, "o", torch.bfloat16), lp, B, H, Tq, Tkv, d,
+                              int(bool(causal)), scale, int(kv_chunk), wp, wbytes, _stream())
     _check(st)
     return (o, lse) if return_lse else o
 
@@ -203,18 +230,28 @@ def attn_status_string(status: int) -> str:
     return lib().attn_status_string(int(status)).decode()
 
 
-def prepared_fwd(q, k, v, o, lse, causal: bool, scale: float | None = None, f32: bool = False):
-    """A zero-argument callable that enqueues attn_fwd (or attn_fwd_f32) on
-    the current stream with these tensors; argument checks happen once here,
-    so repeated launches (benchmark loops) cost only the C call."""
+def prepared_fwd(q, k, v, o, lse, causal: bool, scale: float | None = None, f32: bool = False,
+                 kv_chunk: int | None = None, workspace=None):
+    """A zero-argument callable that enqueues attn_fwd (or attn_fwd_f32, or
+    attn_fwd_split when ``kv_chunk`` is given) on the current stream with these
+    tensors; argument checks happen once here, so repeated launches
+    (benchmark loops) cost only the C call."""
     B, H, Tq, Tkv, d = _shape4(q, k, v)
     dt = torch.float32 if f32 else torch.bfloat16
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     ptrs = [_dev(t, n, dt) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"))]
     lp = None if lse is None else _dev(lse, "lse", torch.float32)
-    fn = lib().attn_fwd_f32 if f32 else lib().attn_fwd
     stream = _stream()
-    args = (*ptrs, lp, B, H, Tq, Tkv, d, int(bool(causal)), scale, stream)
+    if kv_chunk is not None:
+        if f32:
+            raise ValueError("the split forward is bf16")
+        wp, wb = (None, 0) if workspace is None else (_dev(workspace, "workspace", workspace.dtype),
+                                                      workspace.numel() * workspace.element_size())
+        fn = lib().attn_fwd_split
+        args = (*ptrs, lp, B, H, Tq, Tkv, d, int(bool(causal)), scale, int(kv_chunk), wp, wb, stream)
+    else:
+        fn = lib().attn_fwd_f32 if f32 else lib().attn_fwd
+        args = (*ptrs, lp, B, H, Tq, Tkv, d, int(bool(causal)), scale, stream)
 
     def call():
         _check(fn(*args))

@@ -101,6 +101,57 @@ int run_decode(const void* q, const void* k, const void* v, void* o, float* lse,
     return finish(attn::launch_decode_bf16(a, stream, &name), name);
 }
 
+// The workspace must be 16-byte aligned and overlap none of the tensors.
+int check_workspace(const void* ws, size_t need, const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, uint64_t qbytes, uint64_t kvbytes, uint64_t lsebytes) {
+    if (!aligned(ws, 16)) return fail(ATTN_EINVAL, "workspace must be 16-byte aligned");
+    const uintptr_t w0 = reinterpret_cast<uintptr_t>(ws), w1 = w0 + need;
+    const uintptr_t ptrs[4] = {reinterpret_cast<uintptr_t>(q), reinterpret_cast<uintptr_t>(k),
+                               reinterpret_cast<uintptr_t>(v), reinterpret_cast<uintptr_t>(o)};
+    const uint64_t lens[4] = {qbytes, kvbytes, kvbytes, qbytes};
+    for (int i = 0; i < 4; ++i)
+        if (w0 < ptrs[i] + lens[i] && ptrs[i] < w1) return fail(ATTN_EINVAL, "workspace overlaps a tensor");
+    if (lse) {
+        const uintptr_t l0 = reinterpret_cast<uintptr_t>(lse), l1 = l0 + lsebytes;
+        if (w0 < l1 && l0 < w1) return fail(ATTN_EINVAL, "workspace overlaps lse");
+    }
+    return ATTN_OK;
+}
+
+// bf16 forward; `split` selects the work-unit plan (no split for attn_fwd).
+int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Tq, int Tkv,
+            int d, int causal, float scale, const attn::PrefillSplit& split, void* ws, hipStream_t stream) {
+    if (Tq == 1) {
+        // a single query row: the decode kernel, unsplit (bottom-right causal
+        // alignment lets the one row see every key, so causal changes nothing)
+        return run_decode(q, k, v, o, lse, B, H, H, Tkv, d, scale, 1, nullptr, stream);
+    }
+    attn::PrefillArgs a{q, k, v, o, lse, B, H, Tq, Tkv, d, causal != 0, float(double(scale) * kLog2e), ws};
+    const char* name = nullptr;
+    (void)hipGetLastError();
+    return finish(attn::launch_prefill_bf16_d64(a, split, stream, &name), name);
+}
+
+// Shape checks of the bf16 forward beyond check_common.
+int check_fwd_shape(int B, int H, int Tq, int Tkv, int d) {
+    if (Tq == 1) {
+        if (d != 64 && d != 128) return fail(ATTN_EUNSUPPORTED, "bf16 single-query path supports d in {64, 128}");
+        return ATTN_OK;
+    }
+    if (d != 64) return fail(ATTN_EUNSUPPORTED, "bf16 prefill supports d = 64");
+    if (!attn::prefill_bf16_fits(Tkv)) return fail(ATTN_EUNSUPPORTED, "bf16 prefill supports Tkv*d*2 < 2^31 bytes per head");
+    if (double(B) * H * ((Tq + 127) / 128) > 2147483647.0) return fail(ATTN_EINVAL, "grid too large");
+    return ATTN_OK;
+}
+
+// The split plan of attn_fwd_split, or no split when the shape has none.
+attn::PrefillSplit fwd_split_plan(int B, int H, int Tq, int Tkv, int d, int causal, int kv_chunk) {
+    if (Tq == 1 || d != 64) return attn::PrefillSplit{0, 1, 0};
+    attn::PrefillSplit p = attn::prefill_bf16_split_plan(B, H, Tq, Tkv, causal != 0, kv_chunk);
+    if (double(B) * H * ((Tq + 127) / 128) * p.nch_max > 2147483647.0) return attn::PrefillSplit{0, 1, 0};
+    return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -109,20 +160,37 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
              int d, int causal, float scale, hipStream_t stream) {
     int st = check_common(q, k, v, o, lse, B, H, H, Tq, Tkv, d, causal, scale, 2);
     if (st != ATTN_OK) return st;
-    if (Tq == 1) {
-        // a single query row: the decode kernel, unsplit (bottom-right causal
-        // alignment lets the one row see every key, so causal changes nothing)
-        if (d != 64 && d != 128) return fail(ATTN_EUNSUPPORTED, "bf16 single-query path supports d in {64, 128}");
-        return run_decode(q, k, v, o, lse, B, H, H, Tkv, d, scale, 1, nullptr, stream);
-    }
-    if (d != 64) return fail(ATTN_EUNSUPPORTED, "bf16 prefill supports d = 64");
-    if (!attn::prefill_bf16_fits(Tkv)) return fail(ATTN_EUNSUPPORTED, "bf16 prefill supports Tkv*d*2 < 2^31 bytes per head");
-    if (double(B) * H * ((Tq + 127) / 128) > 2147483647.0) return fail(ATTN_EINVAL, "grid too large");
-    attn::PrefillArgs a{q, k, v, o, lse, B, H, Tq, Tkv, d, causal != 0, float(double(scale) * kLog2e)};
-    const char* name = nullptr;
-    (void)hipGetLastError();
-    return finish(attn::launch_prefill_bf16_d64(a, stream, &name), name);
+    if ((st = check_fwd_shape(B, H, Tq, Tkv, d)) != ATTN_OK) return st;
+    return run_fwd(q, k, v, o, lse, B, H, Tq, Tkv, d, causal, scale, attn::PrefillSplit{0, 1, 0}, nullptr, stream);
 }
+
+size_t attn_fwd_split_workspace_bytes(int B, int H, int Tq, int Tkv, int d, int causal, int kv_chunk) {
+    if (B < 1 || H < 1 || Tq < 1 || Tkv < 1 || d < 1 || (causal != 0 && causal != 1) || kv_chunk < 0) return 0;
+    if (causal && Tq > Tkv) return 0;
+    return fwd_split_plan(B, H, Tq, Tkv, d, causal, kv_chunk).workspace_bytes;
+}
+
+int attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Tq, int Tkv,
+                   int d, int causal, float scale, int kv_chunk, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+    int st = check_common(q, k, v, o, lse, B, H, H, Tq, Tkv, d, causal, scale, 2);
+    if (st != ATTN_OK) return st;
+    if (kv_chunk < 0) return fail(ATTN_EINVAL, "kv_chunk must be >= 0");
+    if ((st = check_fwd_shape(B, H, Tq, Tkv, d)) != ATTN_OK) return st;
+    const attn::PrefillSplit plan = fwd_split_plan(B, H, Tq, Tkv, d, causal, kv_chunk);
+    if (plan.nch_max > 1) {
+        if (!workspace) return fail(ATTN_EWORKSPACE, "workspace is NULL");
+        if (workspace_bytes < plan.workspace_bytes)
+            return fail(ATTN_EWORKSPACE, "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " +
+                                             std::to_string(plan.workspace_bytes));
+        const uint64_t qb = uint64_t(B) * H * Tq * d * 2, kvb = uint64_t(B) * H * Tkv * d * 2;
+        if ((st = check_workspace(workspace, plan.workspace_bytes, q, k, v, o, lse, qb, kvb,
+                                  uint64_t(B) * H * Tq * 4)) != ATTN_OK)
+            return st;
+    }
+    return run_fwd(q, k, v, o, lse, B, H, Tq, Tkv, d, causal, scale, plan, workspace, stream);
+}
+
 
 int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int Tq,
                  int Tkv, int d, int causal, float scale, hipStream_t stream) {
@@ -130,7 +198,7 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
     if (st != ATTN_OK) return st;
     if (!attn::prefill_f32_supports(d)) return fail(ATTN_EUNSUPPORTED, "fp32 path supports d in {16, 32, 64, 128}");
     if (double(B) * H * Tq > 2147483647.0) return fail(ATTN_EINVAL, "grid too large");
-    attn::PrefillArgs a{q, k, v, o, lse, B, H, Tq, Tkv, d, causal != 0, float(double(scale) * kLog2e)};
+    attn::PrefillArgs a{q, k, v, o, lse, B, H, Tq, Tkv, d, causal != 0, float(double(scale) * kLog2e), nullptr};
     const char* name = nullptr;
     (void)hipGetLastError();
     return finish(attn::launch_prefill_f32(a, stream, &name), name);
@@ -156,18 +224,9 @@ int attn_decode_gqa(const void* q, const void* k, const void* v, void* o, float*
         if (workspace_bytes < need)
             return fail(ATTN_EWORKSPACE, "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " +
                                              std::to_string(need));
-        if (!aligned(workspace, 16)) return fail(ATTN_EINVAL, "workspace must be 16-byte aligned");
-        const uintptr_t w0 = reinterpret_cast<uintptr_t>(workspace), w1 = w0 + need;
         const uint64_t kvb = uint64_t(B) * Hkv * Tkv * d * 2, qb = uint64_t(B) * Hq * d * 2;
-        const uintptr_t ptrs[4] = {reinterpret_cast<uintptr_t>(q), reinterpret_cast<uintptr_t>(k),
-                                   reinterpret_cast<uintptr_t>(v), reinterpret_cast<uintptr_t>(o)};
-        const uint64_t lens[4] = {qb, kvb, kvb, qb};
-        for (int i = 0; i < 4; ++i)
-            if (w0 < ptrs[i] + lens[i] && ptrs[i] < w1) return fail(ATTN_EINVAL, "workspace overlaps a tensor");
-        if (lse) {
-            const uintptr_t l0 = reinterpret_cast<uintptr_t>(lse), l1 = l0 + uint64_t(B) * Hq * 4;
-            if (w0 < l1 && l0 < w1) return fail(ATTN_EINVAL, "workspace overlaps lse");
-        }
+        if ((st = check_workspace(workspace, need, q, k, v, o, lse, qb, kvb, uint64_t(B) * Hq * 4)) != ATTN_OK)
+            return st;
     }
     return run_decode(q, k, v, o, lse, B, Hq, Hkv, Tkv, d, scale, splits, workspace, stream);
 }

@@ -15,7 +15,16 @@ struct PrefillArgs {
     float* lse;
     int B, H, Tq, Tkv, d;
     bool causal;
-    float c;   // scale * log2(e)
+    float c;          // scale * log2(e)
+    void* workspace;  // split partials (prefill_bf16 with a split plan), else unused
+};
+
+// How a bf16 prefill is divided into work units: tiles whose key range is
+// longer than `chunk` blocks of 64 keys are split into near-equal chunks.
+struct PrefillSplit {
+    int chunk;               // blocks per unit (0 = no split)
+    int nch_max;             // chunks of the longest tile (1 = no split)
+    size_t workspace_bytes;  // partials: B*H*tiles*nch_max*128*(d+1) floats
 };
 
 struct DecodeArgs {
@@ -30,7 +39,9 @@ struct DecodeArgs {
     void* workspace;  // B*H*num_splits*(d+2) floats, unused when num_splits == 1
 };
 
-hipError_t launch_prefill_bf16_d64(const PrefillArgs& a, hipStream_t stream, const char** name);
+PrefillSplit prefill_bf16_split_plan(int B, int H, int Tq, int Tkv, bool causal, int kv_chunk);
+hipError_t launch_prefill_bf16_d64(const PrefillArgs& a, const PrefillSplit& split, hipStream_t stream,
+                                   const char** name);
 bool prefill_bf16_fits(int Tkv);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream, const char** name);
 bool prefill_f32_supports(int d);

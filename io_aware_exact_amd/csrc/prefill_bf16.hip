@@ -48,6 +48,8 @@
 // * Tiles are launched heaviest-first (last query tiles first) and the
 //   linear block id keeps every tile of one (batch, head) on one XCD when the
 //   number of heads is a multiple of 8.
+#include <cstdio>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -64,11 +66,29 @@ constexpr float kSumLimit = 65536.0f;         // 2^16: largest block row sum kep
 __device__ __forceinline__ int swz_k(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int swz_v(int row) { return ((row >> 1) & 1) << 2; }
 
+// Key blocks a query tile must visit (causal: up to its last row's diagonal).
+__host__ __device__ __forceinline__ int tile_blocks(int qt, int bq, int Tq, int Tkv, bool causal) {
+    const int kend = causal ? min(Tkv, (qt + 1) * bq + (Tkv - Tq)) : Tkv;
+    return (kend + BK - 1) / BK;
+}
+
+// Chunks a tile of nblk key blocks is split into when a work unit takes at
+// most `chunk` blocks (chunk <= 0: never split).
+__host__ __device__ __forceinline__ int tile_chunks(int nblk, int chunk) {
+    return chunk > 0 ? (nblk + chunk - 1) / chunk : 1;
+}
+
+// One work unit = one query tile x one chunk of its key blocks.  Chunk cc of a
+// tile split into nch chunks covers blocks [cc*nblk/nch, (cc+1)*nblk/nch).
+// Units of unsplit tiles write O and LSE; units of split tiles write their
+// partial result (O normalised by the chunk's own sum, and the chunk's
+// base-2 log-sum-exp) to `part`, merged later by prefill_combine_kernel.
 template <int WAVES, int NS, bool CAUSAL>
 __global__ __launch_bounds__(WAVES * 64, 2)
 void prefill_bf16_d64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                              const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                             float* __restrict__ LSE, int Tq, int Tkv, int BH, int nqt, float c) {
+                             float* __restrict__ LSE, float* __restrict__ part, int Tq, int Tkv, int BH,
+                             int nqt, int chunk, int nch_max, float c) {
     constexpr int BQ = WAVES * 32;
     static_assert(8 % WAVES == 0, "row groups of a block must split evenly over the waves");
     constexpr int LI = 8 / WAVES;             // 1 KiB load instructions per wave per operand per block
@@ -81,12 +101,23 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __r
     const int ln = lane & 31;
     const int hf = lane >> 5;
 
+    // unit id = (cc * nqt + rank) * BH + bh: first chunks of every tile first,
+    // heaviest tiles first within a chunk index, and all units of one
+    // (batch, head) on one XCD when BH is a multiple of 8
     const int id = blockIdx.x;
     const int bh = id % BH;
-    const int rank = id / BH;
+    const int rest = id / BH;
+    const int rank = rest % nqt;
+    const int cc = rest / nqt;
     const int qt = CAUSAL ? (nqt - 1 - rank) : rank;
     const int q0 = qt * BQ;
     const int off = Tkv - Tq;                 // bottom-right causal alignment
+
+    const int nblk = tile_blocks(qt, BQ, Tq, Tkv, CAUSAL);
+    const int nch = tile_chunks(nblk, chunk);
+    if (cc >= nch) return;                    // this tile has fewer chunks (uniform per workgroup)
+    const int jlo = (int)(((long long)cc * nblk) / nch);
+    const int jhi = (int)(((long long)(cc + 1) * nblk) / nch);
 
     const size_t qbase = (size_t)bh * Tq * D;
     const size_t kvbase = (size_t)bh * Tkv * D;
@@ -105,8 +136,6 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __r
         for (int t = 0; t < 4; ++t) qf[t] = __builtin_bit_cast(bf16x8_t, u32x4_t{0, 0, 0, 0});
     }
 
-    const int kend = CAUSAL ? min(Tkv, q0 + BQ + off) : Tkv;
-    const int nblk = (kend + BK - 1) / BK;
     const int wq_first = q0 + wave * 32;       // this wave's first / last query row
     const int wq_last = wq_first + 31;
     const int lim = CAUSAL ? min(Tkv - 1, qrow + off) : (Tkv - 1);   // last key this row may see
@@ -121,11 +150,11 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __r
         k_voff[i] = (uint32_t)(row * ROWB + ((slot ^ swz_k(row)) << 4));
         v_voff[i] = (uint32_t)(row * ROWB + ((slot ^ swz_v(row)) << 4));
     }
-    // Block j goes to stage j % NS.  Blocks past the end still issue (empty
-    // range, no memory traffic) so that every wave's vmcnt stays uniform.
+    // Block j goes to stage j % NS.  Blocks past the unit's end still issue
+    // (empty range, no memory traffic) so that every wave's vmcnt stays uniform.
     auto issue = [&](int j) {
         const int kb = j * BK;
-        const bool live = kb < Tkv;
+        const bool live = j < jhi;
         const uint32_t bytes = live ? (uint32_t)(Tkv - kb) * (uint32_t)ROWB : 0u;
         const size_t eoff = live ? (size_t)kb * D : 0;
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + eoff, bytes);
@@ -256,16 +285,17 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __r
     const int nfull = CAUSAL ? min(Tkv / BK, (q0 + off + 1) / BK) : Tkv / BK;
 
 #pragma unroll
-    for (int j = 0; j < NS - 1; ++j) issue(j);
+    for (int j = 0; j < NS - 1; ++j) issue(jlo + j);
 
-    int j = 0;
-    for (; j < nfull; ++j) {
+    int j = jlo;
+    const int jfull = min(nfull, jhi);
+    for (; j < jfull; ++j) {
         wait_vmcnt<2 * LI * (NS - 2)>();      // this wave's part of block j has landed
         __syncthreads();                      // ... everyone's, and stage (j-1) % NS is free
         issue(j + NS - 1);
         step(&ring[j % NS][0][0], j * BK, std::false_type{});
     }
-    for (; j < nblk; ++j) {
+    for (; j < jhi; ++j) {
         wait_vmcnt<2 * LI * (NS - 2)>();
         __syncthreads();
         issue(j + NS - 1);
@@ -276,6 +306,31 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __r
 
     // ---- epilogue: divide once, write O (bf16) and LSE (fp32) ----
     const float lsum = half_swap_sum(l);
+    if (nch > 1) {
+        // partial of a split tile; a row may see no key of a later chunk
+        // (causal), then its weight is zero: o = 0, lse2 = -inf
+        if (qrow < Tq) {
+            const size_t rec = ((size_t)bh * nqt + qt) * nch_max + cc;
+            float* prow = part + (rec * BQ + (qrow - q0)) * D;
+            const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    float4 w;
+                    w.x = oacc[dt][4 * g] * inv;
+                    w.y = oacc[dt][4 * g + 1] * inv;
+                    w.z = oacc[dt][4 * g + 2] * inv;
+                    w.w = oacc[dt][4 * g + 3] * inv;
+                    *reinterpret_cast<float4*>(prow + 32 * dt + 8 * g + 4 * hf) = w;
+                }
+            if (hf == 0) {
+                float* plse = part + (size_t)BH * nqt * nch_max * BQ * D;
+                plse[rec * BQ + (qrow - q0)] = lsum > 0.f ? m + __builtin_log2f(lsum) : kNegInf;
+            }
+        }
+        return;
+    }
     if (qrow < Tq) {
         const float inv = 1.0f / lsum;
         uint16_t* orow = O + qbase + (size_t)qrow * D;
@@ -292,18 +347,90 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __r
     }
 }
 
-template <int WAVES, int NS, bool CAUSAL>
-hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
-    constexpr int BQ = WAVES * 32;
-    const int nqt = (a.Tq + BQ - 1) / BQ;
-    const long long grid = (long long)nqt * a.B * a.H;
+// Merge the chunk partials of each split tile: for row r with chunk results
+// (O_c, lse2_c), M = max_c lse2_c, w_c = 2^(lse2_c - M),
+// O = sum_c w_c O_c / sum_c w_c and LSE = (M + log2 sum_c w_c) ln 2 -- the
+// rescaling merge of "IO-Aware Attention", section "Parallelism and the cost
+// of the split", applied online over groups of CG chunks so that every load
+// of a group is in flight at once.  blockIdx.x = tile (qt * BH + bh, the XCD
+// of the tile's units), blockIdx.y = a slice of 16 rows; each thread owns 4
+// columns of one row.
+constexpr int CG = 4;
+
+template <int BQ>
+__global__ __launch_bounds__(256)
+void prefill_combine_kernel(const float* __restrict__ part, uint16_t* __restrict__ O, float* __restrict__ LSE,
+                            int Tq, int Tkv, int BH, int nqt, int chunk, int nch_max, int causal) {
+    const int bh = blockIdx.x % BH;
+    const int qt = blockIdx.x / BH;
+    const int nch = tile_chunks(tile_blocks(qt, BQ, Tq, Tkv, causal != 0), chunk);
+    if (nch <= 1) return;
+    const int r = blockIdx.y * 16 + (threadIdx.x >> 4);
+    const int col = 4 * (threadIdx.x & 15);
+    const int qrow = qt * BQ + r;
+    if (qrow >= Tq) return;
+    const size_t rec0 = ((size_t)bh * nqt + qt) * nch_max;
+    const float* plse = part + (size_t)BH * nqt * nch_max * BQ * D;
+    float M = kNegInf, L = 0.f;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < nch; k0 += CG) {
+        float lk[CG];
+        float4 x[CG];
+#pragma unroll
+        for (int i = 0; i < CG; ++i) {
+            const int k = min(k0 + i, nch - 1);   // repeats of the last chunk get weight 0 below
+            lk[i] = plse[(rec0 + k) * BQ + r];
+            x[i] = *reinterpret_cast<const float4*>(part + ((rec0 + k) * BQ + r) * D + col);
+        }
+        float mg = M;
+#pragma unroll
+        for (int i = 0; i < CG; ++i)
+            if (k0 + i < nch) mg = fmaxf(mg, lk[i]);
+        const float alpha = fast_exp2(M - mg);   // M = -inf on the first group: alpha = 0
+        L *= alpha;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] *= alpha;
+#pragma unroll
+        for (int i = 0; i < CG; ++i) {
+            const float w = (k0 + i < nch) ? fast_exp2(lk[i] - mg) : 0.f;
+            L += w;
+            acc[0] = __builtin_fmaf(w, x[i].x, acc[0]);
+            acc[1] = __builtin_fmaf(w, x[i].y, acc[1]);
+            acc[2] = __builtin_fmaf(w, x[i].z, acc[2]);
+            acc[3] = __builtin_fmaf(w, x[i].w, acc[3]);
+        }
+        M = mg;
+    }
+    const float inv = 1.0f / L;
+    const u32x2_t w = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+    *reinterpret_cast<u32x2_t*>(O + ((size_t)bh * Tq + qrow) * D + col) = w;
+    if (LSE != nullptr && col == 0)
+        LSE[(size_t)bh * Tq + qrow] = (M + __builtin_log2f(L)) * 0.69314718055994530942f;
+}
+
+constexpr int kWaves = 4;
+constexpr int kStages = 3;
+constexpr int kBQ = kWaves * 32;
+
+template <bool CAUSAL>
+hipError_t launch_one(const PrefillArgs& a, int chunk, int nch_max, hipStream_t stream) {
+    const int nqt = (a.Tq + kBQ - 1) / kBQ;
+    const long long tiles = (long long)nqt * a.B * a.H;
+    const long long grid = tiles * nch_max;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((prefill_bf16_d64_kernel<WAVES, NS, CAUSAL>), dim3((unsigned)grid), dim3(WAVES * 64), 0,
-                       stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, a.Tq, a.Tkv,
-                       a.B * a.H, nqt, a.c);
+    hipLaunchKernelGGL((prefill_bf16_d64_kernel<kWaves, kStages, CAUSAL>), dim3((unsigned)grid), dim3(kWaves * 64),
+                       0, stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                       static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
+                       static_cast<float*>(a.workspace), a.Tq, a.Tkv, a.B * a.H, nqt, chunk, nch_max, a.c);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || nch_max <= 1) return e;
+    hipLaunchKernelGGL((prefill_combine_kernel<kBQ>), dim3((unsigned)tiles, kBQ / 16), dim3(256), 0, stream,
+                       static_cast<const float*>(a.workspace), static_cast<uint16_t*>(a.o), a.lse, a.Tq, a.Tkv,
+                       a.B * a.H, nqt, chunk, nch_max, a.causal ? 1 : 0);
     return hipGetLastError();
 }
+
+thread_local char g_name[128];
 
 }  // namespace
 
@@ -312,13 +439,52 @@ bool prefill_bf16_fits(int Tkv) {
     return (long long)Tkv * D * 2 < (1LL << 31);
 }
 
-hipError_t launch_prefill_bf16_d64(const PrefillArgs& a, hipStream_t stream, const char** name) {
-    if (a.causal) {
-        *name = "prefill_bf16_d64<waves=4,bq=128,bk=64,stages=3,causal>";
-        return launch_one<4, 3, true>(a, stream);
+PrefillSplit prefill_bf16_split_plan(int B, int H, int Tq, int Tkv, bool causal, int kv_chunk) {
+    PrefillSplit p{0, 1, 0};
+    const int nqt = (Tq + kBQ - 1) / kBQ;
+    int maxb = 0;
+    long long total = 0;
+    for (int qt = 0; qt < nqt; ++qt) {
+        const int nb = tile_blocks(qt, kBQ, Tq, Tkv, causal);
+        maxb = nb > maxb ? nb : maxb;
+        total += nb;
     }
-    *name = "prefill_bf16_d64<waves=4,bq=128,bk=64,stages=3>";
-    return launch_one<4, 3, false>(a, stream);
+    int chunk = 0;
+    if (kv_chunk > 0) {
+        chunk = (kv_chunk + BK - 1) / BK;
+    } else {
+        // automatic: split only when the query tiles alone leave the chip
+        // short of work (fewer than 3 resident tiles per compute unit), with
+        // units of an even share of all key blocks over 768 slots but never
+        // under 16 blocks -- a unit pays a few microseconds of start-up
+        // latency plus its partial's round trip, which shorter units do not
+        // earn back (measured on 1-16 heads of 1K-16K keys).
+        const long long slots = 3LL * 256;
+        const long long tiles = (long long)nqt * B * H;
+        if (tiles < slots) {
+            const long long share = (total * B * H + slots - 1) / slots;
+            chunk = (int)(share < 16 ? 16 : share);
+        }
+    }
+    if (chunk <= 0 || chunk >= maxb) return p;
+    p.chunk = chunk;
+    p.nch_max = tile_chunks(maxb, chunk);
+    p.workspace_bytes = (size_t)B * H * nqt * p.nch_max * kBQ * (D + 1) * sizeof(float);
+    return p;
+}
+
+hipError_t launch_prefill_bf16_d64(const PrefillArgs& a, const PrefillSplit& sp, hipStream_t stream,
+                                   const char** name) {
+    if (sp.nch_max > 1)
+        snprintf(g_name, sizeof g_name, "prefill_bf16_d64<waves=4,bq=128,bk=64,stages=3%s,kv_chunk=%d>+combine",
+                 a.causal ? ",causal" : "", sp.chunk * BK);
+    else
+        snprintf(g_name, sizeof g_name, "prefill_bf16_d64<waves=4,bq=128,bk=64,stages=3%s>",
+                 a.causal ? ",causal" : "");
+    *name = g_name;
+    const int chunk = sp.nch_max > 1 ? sp.chunk : 0;
+    if (a.causal) return launch_one<true>(a, chunk, sp.nch_max, stream);
+    return launch_one<false>(a, chunk, sp.nch_max, stream);
 }
 
 }  // namespace attn

@@ -71,6 +71,10 @@ WORKLOADS = {
     "mid_causal": Workload("mid_causal", 2, 16, 4096, 4096, 64, "bf16", True, seed=3, k_factor=3.0),
     # long-context causal prefill
     "long": Workload("long", 1, 12, 16384, 16384, 64, "bf16", True, seed=4),
+    # one head of a 16K-token sequence (batch 1): too few query tiles to fill
+    # the chip, the case for splitting the key axis of prefill
+    "long_1head": Workload("long_1head", 1, 1, 16384, 16384, 64, "bf16", True, seed=7),
+    "long_1head_full": Workload("long_1head_full", 1, 1, 16384, 16384, 64, "bf16", False, seed=8),
     # one query per sequence against 8,192 cached keys, split-KV into 16 chunks
     "decode": Workload("decode", 64, 32, 1, 8192, 128, "bf16", False, seed=5, num_splits=16),
     # the same decode step with grouped-query attention: 32 query heads over

@@ -65,6 +65,14 @@ def dec(lib, **kw):
                            a["P"], a["ws"], a["wsb"], a["stream"])
 
 
+def fsplit(lib, **kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, B=4, H=12, Tq=1024, Tkv=1024, d=64, causal=1, scale=0.125, chunk=256,
+             ws=W, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.attn_fwd_split(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Tq"], a["Tkv"], a["d"],
+                              a["causal"], a["scale"], a["chunk"], a["ws"], a["wsb"], a["stream"])
+
+
 def gqa(lib, **kw):
     a = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, Hq=8, Hkv=2, Tkv=100, d=128, scale=0.088, P=4, ws=W, wsb=1 << 30,
              stream=None)
@@ -73,7 +81,7 @@ def gqa(lib, **kw):
                                a["d"], a["scale"], a["P"], a["ws"], a["wsb"], a["stream"])
 
 
-@pytest.mark.parametrize("call", [fwd, fwd32])
+@pytest.mark.parametrize("call", [fwd, fwd32, fsplit])
 @pytest.mark.parametrize("bad, want", [
     (dict(q=None), "q is NULL"), (dict(k=None), "k is NULL"), (dict(v=None), "v is NULL"),
     (dict(o=None), "o is NULL"),
@@ -127,6 +135,39 @@ def test_gqa_decode_arguments(lib):
     kv_bytes = 2 * 2 * 100 * 128 * 2
     assert gqa(lib, o=K + kv_bytes - 256) == EINVAL and "o overlaps k" in attn.attn_status_string(EINVAL)
     assert gqa(lib, ws=K + kv_bytes - 64) == EINVAL and "overlaps" in attn.attn_status_string(EINVAL)
+
+
+def test_split_forward_arguments(lib):
+    assert fsplit(lib, chunk=-1) == EINVAL and "kv_chunk" in attn.attn_status_string(EINVAL)
+    assert fsplit(lib, ws=None) == EWS and "NULL" in attn.attn_status_string(EWS)
+    need = attn.attn_fwd_split_workspace_bytes(4, 12, 1024, 1024, 64, True, 256)
+    assert fsplit(lib, wsb=need - 1) == EWS and str(need) in attn.attn_status_string(EWS)
+    assert fsplit(lib, ws=W + 8) == EINVAL and "aligned" in attn.attn_status_string(EINVAL)
+    assert fsplit(lib, ws=V + 4096) == EINVAL and "overlaps" in attn.attn_status_string(EINVAL)
+    assert fsplit(lib, d=128) == EUNSUP
+
+
+def test_split_forward_workspace_formula():
+    # 8 query tiles of 128 rows; the longest (1024 keys) splits into 4 chunks of 256
+    per_unit = 128 * (64 + 1) * 4
+    assert attn.attn_fwd_split_workspace_bytes(4, 12, 1024, 1024, 64, True, 256) == 4 * 12 * 8 * 4 * per_unit
+    assert attn.attn_fwd_split_workspace_bytes(4, 12, 1024, 1024, 64, False, 320) == 4 * 12 * 8 * 4 * per_unit
+    # a chunk covering the longest tile, or a single key block, means no split
+    assert attn.attn_fwd_split_workspace_bytes(4, 12, 1024, 1024, 64, True, 1024) == 0
+    assert attn.attn_fwd_split_workspace_bytes(1, 1, 300, 17, 64, False, 64) == 0
+    # automatic choice: many tiles -> no split; tiles of at most 1024 keys -> no split;
+    # few long tiles -> split into units of an even share (here 1 head of 16K causal
+    # keys: 16512 blocks / 768 -> 22 blocks, 256-block tiles -> 12 chunks)
+    assert attn.attn_fwd_split_workspace_bytes(1, 12, 16384, 16384, 64, True, 0) == 0
+    assert attn.attn_fwd_split_workspace_bytes(4, 12, 1024, 1024, 64, True, 0) == 0
+    assert attn.attn_fwd_split_workspace_bytes(1, 1, 16384, 16384, 64, True, 0) == 1 * 128 * 12 * per_unit
+    # 2 heads of 8K causal keys: share 11 -> 16 blocks; the 128-block tiles -> 8 chunks
+    assert attn.attn_fwd_split_workspace_bytes(1, 2, 8192, 8192, 64, True, 0) == 2 * 64 * 8 * per_unit
+    # invalid or unsupported -> 0
+    assert attn.attn_fwd_split_workspace_bytes(4, 12, 1024, 1024, 64, True, -1) == 0
+    assert attn.attn_fwd_split_workspace_bytes(4, 12, 1024, 1024, 128, True, 256) == 0
+    assert attn.attn_fwd_split_workspace_bytes(4, 12, 1, 1024, 64, False, 256) == 0
+    assert attn.attn_fwd_split_workspace_bytes(4, 12, 2048, 1024, 64, True, 256) == 0
 
 
 def test_workspace_size_formula():

@@ -154,6 +154,73 @@ def test_prefill_fp32_shapes(d, Tq, Tkv, causal):
                         seed=5 + d + Tq))
 
 
+SPLIT_CASES = [
+    # B, H, Tq, Tkv, causal, kv_chunk
+    (1, 2, 1000, 1000, True, 64),     # one block per unit
+    (1, 2, 1000, 1000, True, 256),
+    (2, 3, 129, 129, True, 64),       # ragged last tile
+    (1, 2, 100, 300, True, 64),       # bottom-right causal, Tq < Tkv
+    (1, 2, 100, 300, False, 128),
+    (1, 1, 257, 1000, False, 192),    # chunk not a multiple of the block: rounded up
+    (1, 1, 33, 700, True, 64),
+    (3, 1, 1000, 1000, True, 0),      # automatic choice
+    (1, 1, 300, 17, False, 64),       # one key block: nothing to split
+    (1, 3, 5, 1, False, 64),
+]
+
+
+@pytest.mark.parametrize("B,H,Tq,Tkv,causal,chunk", SPLIT_CASES)
+def test_prefill_split_shapes(B, H, Tq, Tkv, causal, chunk):
+    w = Workload(f"split[{B},{H},{Tq},{Tkv},{'c' if causal else 'n'},kv={chunk}]", B, H, Tq, Tkv, 64, "bf16",
+                 causal, seed=60 + Tq + Tkv)
+    say(f"case {w}")
+    q, k, v = make_qkv(w)
+    dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
+    o, lse = attn.attn_fwd_split(dq, dk, dv, causal=causal, scale=w.scale, kv_chunk=chunk)
+    torch.cuda.synchronize()
+    kern = attn.attn_last_kernel()
+    say(f"  kernel {kern}")
+    split = attn.attn_fwd_split_workspace_bytes(B, H, Tq, Tkv, 64, causal, chunk) > 0
+    assert ("combine" in kern) == split
+    o_ref, lse_ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), w.scale, causal)
+    compare(w, o, lse, o_ref, lse_ref)
+    o1, lse1 = attn.attn_fwd(dq, dk, dv, causal=causal, scale=w.scale)
+    torch.cuda.synchronize()
+    if not split:
+        assert torch.equal(o, o1) and torch.equal(lse, lse1)
+
+
+def test_gpt2_split_full():
+    w = WORKLOADS["gpt2"]
+    say(f"case {w} (split into 256-key units)")
+    q, k, v = make_qkv(w)
+    o, lse = attn.attn_fwd_split(q.cuda(), k.cuda(), v.cuda(), causal=True, scale=w.scale, kv_chunk=256)
+    torch.cuda.synchronize()
+    kern = attn.attn_last_kernel()
+    say(f"  kernel {kern}")
+    assert "combine" in kern
+    o_ref, lse_ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), w.scale, True)
+    compare(w, o, lse, o_ref, lse_ref)
+
+
+@pytest.mark.parametrize("name", ["long_1head", "long_1head_full"])
+def test_split_full_size_sampled(name):
+    """A single 16K-key head: the automatic plan splits every long tile."""
+    w = WORKLOADS[name]
+    say(f"case {w} (automatic split, sampled rows)")
+    q, k, v = make_qkv(w)
+    o, lse = attn.attn_fwd_split(q.cuda(), k.cuda(), v.cuda(), causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    kern = attn.attn_last_kernel()
+    say(f"  kernel {kern}")
+    assert "combine" in kern
+    rows = _sampled_rows(w.Tq, 64, np.random.default_rng(2000 + w.seed))
+    o_ref, lse_ref = oracle.attention(to_f64(q[0, 0]), to_f64(k[0, 0]), to_f64(v[0, 0]), w.scale, w.causal,
+                                      rows=rows)
+    idx = torch.from_numpy(rows).cuda()
+    compare(w, o[0, 0][idx], lse[0, 0][idx], o_ref, lse_ref, what=f"[{rows.size} rows]")
+
+
 def test_fp32_scores_spread():
     w = WORKLOADS["tiny"].with_(name="tiny_k3", k_factor=3.0)
     full_check(w)
