@@ -11,7 +11,9 @@ online softmax, causal skipping, the epilogue).  The decode half of the path
 (split-KV kernel + combine) is timed the same way on its own workload
 (B=64, H=32, T_kv=8192, d=128, 16 partitions) and reported in "decode", and
 its grouped-query form (the same step with 8 key/value heads for the 32 query
-heads) in "decode_gqa".  "prefill_split" times one 16K-token causal head, a
+heads) in "decode_gqa"; "decode_b1" is one sequence (12 heads of 64, 16K
+keys) with automatically chosen partitions against one partition per head.
+"prefill_split" times one 16K-token causal head, a
 shape with too few query tiles to fill the chip, with and without the key
 axis split across workgroups.
 
@@ -172,11 +174,19 @@ def run_decode(torch, attn, steps, warmup, name="decode"):
     log(f"[bench] {name} inputs ready in {time.perf_counter() - t0:.1f}s")
     o = torch.empty_like(dq)
     lse = torch.empty((w.B, w.H), dtype=torch.float32, device="cuda")
-    ws = torch.empty(attn.attn_decode_workspace_bytes(w.B, w.H, w.d, w.num_splits), dtype=torch.uint8, device="cuda")
-    call = attn.prepared_decode(dq, dk, dv, o, lse, w.num_splits, ws, w.scale)
+    splits = w.num_splits or attn.attn_decode_splits(w.B, w.H, w.kv_heads, w.Tkv, w.d)
+    ws = torch.empty(max(16, attn.attn_decode_workspace_bytes(w.B, w.H, w.d, splits)), dtype=torch.uint8,
+                     device="cuda")
+    total, kv = decode_bytes(w)
+    unsplit = None
+    if w.num_splits == 0:
+        # the same step in one partition per (batch, head): the shape the
+        # pages measured at batch 1
+        ms1 = time_steps(torch, attn.prepared_decode(dq, dk, dv, o, lse, 1, None, w.scale), steps, warmup)
+        unsplit = {"ms_per_step": ms1, "value": total / (ms1 * 1e-3) / 1e9, "kernel": attn.attn_last_kernel()}
+    call = attn.prepared_decode(dq, dk, dv, o, lse, splits, ws, w.scale)
     ms = time_steps(torch, call, steps, warmup)
     kern = attn.attn_last_kernel()
-    total, kv = decode_bytes(w)
     gbps = total / (ms * 1e-3) / 1e9
     # parity on sampled heads (oracle = the definition per head)
     rng = np.random.default_rng(5)
@@ -196,8 +206,9 @@ def run_decode(torch, attn, steps, warmup, name="decode"):
     del dq, dk, dv, q, k, v
     torch.cuda.empty_cache()
     heads = f"H={w.H}" if G == 1 else f"Hq={w.H} Hkv={w.kv_heads}"
-    return {
-        "workload": f"{name} B={w.B} {heads} Tq=1 Tkv={w.Tkv} d={w.d} bf16 splits={w.num_splits}",
+    plan = f"splits={splits}" if w.num_splits else f"splits=auto({splits})"
+    out = {
+        "workload": f"{name} B={w.B} {heads} Tq=1 Tkv={w.Tkv} d={w.d} bf16 {plan}",
         "metric": "decode attention KV-cache read bandwidth",
         "value": gbps,
         "unit": "GB/s",
@@ -212,6 +223,10 @@ def run_decode(torch, attn, steps, warmup, name="decode"):
         "cpu_baseline": {"value": cpu_gbps, "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
                          "sample": f"{sample_heads} (batch, query head) slices, float64 numpy definition"},
     }
+    if unsplit is not None:
+        out["unsplit"] = unsplit
+        out["speedup_vs_unsplit"] = unsplit["ms_per_step"] / ms
+    return out
 
 
 def run_prefill_split(torch, attn, steps, warmup, name="long_1head"):
@@ -351,7 +366,7 @@ def main():
             f"{result['prefill_split']['ms_per_step'] * 1e3:.1f} us/step "
             f"(unsplit {result['prefill_split']['unsplit']['ms_per_step'] * 1e3:.1f} us)")
     if not args.no_decode:
-        for name in ("decode", "decode_gqa"):
+        for name in ("decode", "decode_gqa", "decode_b1"):
             result[name] = run_decode(torch, attn, args.steps, args.warmup, name)
             log(f"[bench] {name} {result[name]['kernel']}: {result[name]['ms_per_step']:.3f} ms/step, "
                 f"{result[name]['value']:.0f} GB/s")

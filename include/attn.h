@@ -49,7 +49,7 @@ extern "C" {
 enum {
     ATTN_OK = 0,
     ATTN_EINVAL = -1,       /* null pointer, size < 1, scale not finite or <= 0, causal with T_q > T_kv,
-                               pointer not 16-byte aligned, num_splits < 1, aliasing output, sizes overflow */
+                               pointer not 16-byte aligned, num_splits < 0, aliasing output, sizes overflow */
     ATTN_EUNSUPPORTED = -2, /* head width d not built for this path */
     ATTN_EHIP = -3,         /* the HIP runtime reported an error while enqueueing */
     ATTN_EWORKSPACE = -4    /* workspace missing or smaller than the call's *_workspace_bytes() */
@@ -126,6 +126,17 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
 size_t attn_decode_workspace_bytes(int B, int H, int d, int num_splits);
 
 /*
+ * attn_decode_splits -- the number of key partitions the library picks for a
+ * decode step (num_splits = 0): enough for about 512 workgroups, at most 32,
+ * and none holding less than 64 KiB of K and V (16384/d keys).  A single sequence offers only H
+ * independent heads, too few to occupy the chip; splitting the key axis is
+ * the remedy "Attention and Its Computational Cost" proposes for its batch-1
+ * decode measurement ("The other shape: one query, many keys").  Returns 0
+ * for invalid or unsupported arguments (d not in {64, 128}, Hq % Hkv != 0).
+ */
+int attn_decode_splits(int B, int Hq, int Hkv, int Tkv, int d);
+
+/*
  * attn_decode -- one query per (batch, head) against T_kv cached keys, with
  * the key axis split into num_splits partitions ("IO-Aware Attention",
  * section "Parallelism and the cost of the split": each partition produces a
@@ -134,8 +145,9 @@ size_t attn_decode_workspace_bytes(int B, int H, int d, int num_splits);
  *
  *   q, o       bf16 [B,H,1,d];  k, v bf16 [B,H,Tkv,d];  lse fp32 [B,H] or NULL
  *   scale      finite and > 0
- *   num_splits >= 1; values above Tkv are clamped to Tkv.  Partition p covers
- *              keys [floor(p*Tkv/P), floor((p+1)*Tkv/P)).
+ *   num_splits >= 1, or 0 for attn_decode_splits(B,H,H,Tkv,d); values above
+ *              Tkv are clamped to Tkv.  Partition p covers keys
+ *              [floor(p*Tkv/P), floor((p+1)*Tkv/P)).
  *   workspace  device memory of at least attn_decode_workspace_bytes(B,H,d,num_splits)
  *              bytes (may be NULL when num_splits == 1); contents on entry are ignored.
  *

@@ -13,6 +13,7 @@ from .attn import (
     AttnError,
     attn_decode,
     attn_decode_gqa,
+    attn_decode_splits,
     attn_decode_workspace_bytes,
     attn_fwd,
     attn_fwd_f32,
@@ -27,7 +28,7 @@ from .attn import (
 
 __all__ = [
     "ATTN_EHIP", "ATTN_EINVAL", "ATTN_EUNSUPPORTED", "ATTN_EWORKSPACE", "ATTN_OK", "AttnError",
-    "attn_decode", "attn_decode_gqa", "attn_decode_workspace_bytes", "attn_fwd", "attn_fwd_f32",
+    "attn_decode", "attn_decode_gqa", "attn_decode_splits", "attn_decode_workspace_bytes", "attn_fwd", "attn_fwd_f32",
     "attn_fwd_split", "attn_fwd_split_workspace_bytes", "attn_last_kernel", "attn_status_string", "lib",
     "prepared_decode", "prepared_fwd",
 ]

@@ -32,6 +32,7 @@ SIGNATURES = {
     "attn_fwd_split": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _S, _P]),
     "attn_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
     "attn_decode_workspace_bytes": (_S, [_I, _I, _I, _I]),
+    "attn_decode_splits": (_I, [_I, _I, _I, _I, _I]),
     "attn_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _S, _P]),
     "attn_decode_gqa": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _S, _P]),
     "attn_last_kernel": (ctypes.c_char_p, []),
@@ -179,10 +180,23 @@ def _workspace(workspace, need: int, device):
     return _dev(workspace, "workspace", workspace.dtype), workspace.numel() * workspace.element_size()
 
 
+def attn_decode_splits(B: int, Hq: int, Hkv: int, Tkv: int, d: int) -> int:
+    return int(lib().attn_decode_splits(B, Hq, Hkv, Tkv, d))
+
+
+def _resolve_splits(num_splits: int, B: int, Hq: int, Hkv: int, Tkv: int, d: int) -> int:
+    """The partition count the library will use (0 = its automatic choice)."""
+    n = int(num_splits)
+    if n == 0:
+        n = attn_decode_splits(B, Hq, Hkv, Tkv, d)
+    return max(1, min(n, Tkv))
+
+
 def attn_decode(q, k, v, scale: float | None = None, num_splits: int = 16, workspace=None, out=None, lse=None,
                 return_lse: bool = True):
     """One query per (batch, head): q [B,H,1,d], k/v [B,H,Tkv,d] -> (o, lse [B,H]).
 
+    ``num_splits`` = 0 lets the library choose (attn_decode_splits);
     ``workspace`` (a uint8 GPU tensor) is allocated when not given.
     """
     B, H, Hkv, Tkv, d = _shape_gqa(q, k, v)
@@ -194,7 +208,7 @@ def attn_decode(q, k, v, scale: float | None = None, num_splits: int = 16, works
     if return_lse and lse is None:
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
     lp = _dev(lse, "lse", torch.float32) if return_lse else None
-    splits = max(1, min(int(num_splits), Tkv))
+    splits = _resolve_splits(num_splits, B, H, H, Tkv, d)
     wp, wbytes = _workspace(workspace, attn_decode_workspace_bytes(B, H, d, splits), q.device)
     st = lib().attn_decode(_dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16), _dev(v, "v", torch.bfloat16),
                            _dev(o, "o", torch.bfloat16), lp, B, H, Tkv, d, scale, int(num_splits), wp, wbytes,
@@ -213,7 +227,7 @@ def attn_decode_gqa(q, k, v, scale: float | None = None, num_splits: int = 16, w
     if return_lse and lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     lp = _dev(lse, "lse", torch.float32) if return_lse else None
-    splits = max(1, min(int(num_splits), Tkv))
+    splits = _resolve_splits(num_splits, B, Hq, Hkv, Tkv, d)
     wp, wbytes = _workspace(workspace, attn_decode_workspace_bytes(B, Hq, d, splits), q.device)
     st = lib().attn_decode_gqa(_dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16),
                                _dev(v, "v", torch.bfloat16), _dev(o, "o", torch.bfloat16), lp, B, Hq, Hkv, Tkv, d,

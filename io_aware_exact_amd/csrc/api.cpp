@@ -214,8 +214,9 @@ int attn_decode_gqa(const void* q, const void* k, const void* v, void* o, float*
                     hipStream_t stream) {
     int st = check_common(q, k, v, o, lse, B, Hq, Hkv, 1, Tkv, d, 0, scale, 2);
     if (st != ATTN_OK) return st;
-    if (num_splits < 1) return fail(ATTN_EINVAL, "num_splits must be >= 1");
+    if (num_splits < 0) return fail(ATTN_EINVAL, "num_splits must be >= 0");
     if (d != 64 && d != 128) return fail(ATTN_EUNSUPPORTED, "decode supports d in {64, 128}");
+    if (num_splits == 0) num_splits = attn::decode_auto_splits(B, Hq, Hkv, Tkv, d);
     const int splits = num_splits > Tkv ? Tkv : num_splits;
     if (splits > 65535) return fail(ATTN_EUNSUPPORTED, "decode supports at most 65535 partitions");
     if (splits > 1) {
@@ -229,6 +230,11 @@ int attn_decode_gqa(const void* q, const void* k, const void* v, void* o, float*
             return st;
     }
     return run_decode(q, k, v, o, lse, B, Hq, Hkv, Tkv, d, scale, splits, workspace, stream);
+}
+
+int attn_decode_splits(int B, int Hq, int Hkv, int Tkv, int d) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Tkv < 1 || (d != 64 && d != 128)) return 0;
+    return attn::decode_auto_splits(B, Hq, Hkv, Tkv, d);
 }
 
 int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Tkv, int d,

@@ -202,7 +202,11 @@ void decode_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     }
 }
 
-// One workgroup of D threads per (batch, query head): merge its P partial records.
+// One workgroup of D threads per (batch, query head): merge its P partial
+// records, online over groups of CG partitions whose loads are all in flight
+// together (the merge is latency-bound, not bandwidth-bound).
+constexpr int CG = 8;
+
 template <int D>
 __global__ __launch_bounds__(D)
 void decode_combine_kernel(const float* __restrict__ part, uint16_t* __restrict__ O,
@@ -210,15 +214,32 @@ void decode_combine_kernel(const float* __restrict__ part, uint16_t* __restrict_
     const int bh = blockIdx.x;
     const int d = threadIdx.x;
     const float* rec = part + (size_t)bh * P * (D + 2);
-    float M = kNegInf;
-    for (int p = 0; p < P; ++p) M = fmaxf(M, rec[(size_t)p * (D + 2) + D]);
-    const float Mu = (M == kNegInf) ? 0.f : M;
-    float L = 0.f, acc = 0.f;
-    for (int p = 0; p < P; ++p) {
-        const float* r = rec + (size_t)p * (D + 2);
-        const float w = fast_exp2(r[D] - Mu);
-        L += w * r[D + 1];
-        acc += w * r[d];
+    float M = kNegInf, L = 0.f, acc = 0.f;
+    for (int p0 = 0; p0 < P; p0 += CG) {
+        float mk[CG], lk[CG], ok[CG];
+#pragma unroll
+        for (int i = 0; i < CG; ++i) {
+            const int p = min(p0 + i, P - 1);   // repeats of the last record get weight 0 below
+            const float* r = rec + (size_t)p * (D + 2);
+            mk[i] = r[D];
+            lk[i] = r[D + 1];
+            ok[i] = r[d];
+        }
+        float mg = M;
+#pragma unroll
+        for (int i = 0; i < CG; ++i)
+            if (p0 + i < P) mg = fmaxf(mg, mk[i]);
+        const float mu = (mg == kNegInf) ? 0.f : mg;
+        const float alpha = fast_exp2(M - mu);
+        L *= alpha;
+        acc *= alpha;
+#pragma unroll
+        for (int i = 0; i < CG; ++i) {
+            const float w = (p0 + i < P) ? fast_exp2(mk[i] - mu) : 0.f;
+            L = __builtin_fmaf(w, lk[i], L);
+            acc = __builtin_fmaf(w, ok[i], acc);
+        }
+        M = mg;
     }
     O[(size_t)bh * D + d] = (uint16_t)(pack_bf16x2(acc / L, 0.f) & 0xffffu);
     if (d == 0 && LSE != nullptr) LSE[bh] = (M + __builtin_log2f(L)) * 0.69314718055994530942f;
@@ -268,6 +289,20 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t stream, const char** name) 
 }
 
 }  // namespace
+
+int decode_auto_splits(int B, int Hq, int Hkv, int Tkv, int d) {
+    // Enough partitions for about 512 workgroups (2 per CU), at most 32, each
+    // holding at least 64 KiB of K and V (256 keys at d = 64, 128 at d = 128):
+    // measured on 12 heads of 64 and 32 heads of 128, batch 1-64, 128-16K
+    // keys, shorter or more numerous partitions lose to their start-up
+    // latency and the merge.
+    const long long wgs = (long long)B * Hkv * (Hq / Hkv / head_tile(Hq / Hkv));
+    const int min_keys = 16384 / d;
+    int p = 1;
+    while (p < 32 && wgs * p < 512) p *= 2;
+    while (p > 1 && Tkv / p < min_keys) p /= 2;
+    return p;
+}
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream, const char** name) {
     if (a.d == 128) return launch_d<128>(a, stream, name);

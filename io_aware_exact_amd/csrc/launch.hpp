@@ -46,5 +46,6 @@ bool prefill_bf16_fits(int Tkv);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream, const char** name);
 bool prefill_f32_supports(int d);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream, const char** name);
+int decode_auto_splits(int B, int Hq, int Hkv, int Tkv, int d);
 
 }  // namespace attn

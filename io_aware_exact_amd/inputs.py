@@ -77,6 +77,9 @@ WORKLOADS = {
     "long_1head_full": Workload("long_1head_full", 1, 1, 16384, 16384, 64, "bf16", False, seed=8),
     # one query per sequence against 8,192 cached keys, split-KV into 16 chunks
     "decode": Workload("decode", 64, 32, 1, 8192, 128, "bf16", False, seed=5, num_splits=16),
+    # one sequence of GPT-2's head shape against 16,384 cached keys (batch 1):
+    # the library picks the number of key partitions
+    "decode_b1": Workload("decode_b1", 1, 12, 1, 16384, 64, "bf16", False, seed=9, num_splits=0),
     # the same decode step with grouped-query attention: 32 query heads over
     # 8 key/value heads (groups of 4), so a quarter of the cache
     "decode_gqa": Workload("decode_gqa", 64, 32, 1, 8192, 128, "bf16", False, seed=6, num_splits=16, Hkv=8),

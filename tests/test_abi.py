@@ -109,7 +109,7 @@ def test_unsupported_head_widths(lib):
 
 
 def test_decode_arguments(lib):
-    assert dec(lib, P=0) == EINVAL and "num_splits" in attn.attn_status_string(EINVAL)
+    assert dec(lib, P=-1) == EINVAL and "num_splits" in attn.attn_status_string(EINVAL)
     assert dec(lib, ws=None) == EWS and "NULL" in attn.attn_status_string(EWS)
     need = attn.attn_decode_workspace_bytes(2, 3, 128, 4)
     assert dec(lib, wsb=need - 1) == EWS and str(need) in attn.attn_status_string(EWS)
@@ -126,7 +126,7 @@ def test_gqa_decode_arguments(lib):
     assert gqa(lib, Hkv=16) == EINVAL
     assert gqa(lib, Hq=0) == EINVAL
     assert gqa(lib, d=96) == EUNSUP
-    assert gqa(lib, P=0) == EINVAL
+    assert gqa(lib, P=-1) == EINVAL
     assert gqa(lib, ws=None) == EWS
     # the workspace is sized by query heads
     need = attn.attn_decode_workspace_bytes(2, 8, 128, 4)
@@ -168,6 +168,25 @@ def test_split_forward_workspace_formula():
     assert attn.attn_fwd_split_workspace_bytes(4, 12, 1024, 1024, 128, True, 256) == 0
     assert attn.attn_fwd_split_workspace_bytes(4, 12, 1, 1024, 64, False, 256) == 0
     assert attn.attn_fwd_split_workspace_bytes(4, 12, 2048, 1024, 64, True, 256) == 0
+
+
+def test_decode_automatic_splits():
+    # 12 heads of one sequence: 512 workgroups would need 43 partitions; capped at 32,
+    # then halved until partitions hold >= 64 KiB of K+V (256 keys at d=64, 128 at d=128)
+    assert attn.attn_decode_splits(1, 12, 12, 16384, 64) == 32
+    assert attn.attn_decode_splits(1, 12, 12, 4096, 64) == 16
+    assert attn.attn_decode_splits(1, 12, 12, 1024, 64) == 4
+    assert attn.attn_decode_splits(1, 12, 12, 300, 64) == 1
+    assert attn.attn_decode_splits(1, 32, 32, 1024, 128) == 8
+    assert attn.attn_decode_splits(16, 12, 12, 16384, 64) == 4    # 192 workgroups -> x4
+    assert attn.attn_decode_splits(64, 32, 32, 8192, 128) == 1    # 2048 workgroups already
+    # grouped-query: workgroups count kv heads x head tiles (groups of 4 -> one tile)
+    assert attn.attn_decode_splits(64, 32, 8, 8192, 128) == 1
+    assert attn.attn_decode_splits(4, 32, 8, 8192, 128) == 16
+    # invalid / unsupported
+    assert attn.attn_decode_splits(1, 12, 5, 1024, 64) == 0
+    assert attn.attn_decode_splits(1, 12, 12, 1024, 96) == 0
+    assert attn.attn_decode_splits(0, 12, 12, 1024, 64) == 0
 
 
 def test_workspace_size_formula():

@@ -229,11 +229,19 @@ def test_fp32_scores_spread():
 @pytest.mark.parametrize("B,H,Tkv,d,splits", [
     (2, 3, 1000, 128, 16), (3, 2, 77, 64, 3), (1, 1, 1, 128, 16), (4, 4, 8192, 64, 16),
     (2, 2, 512, 128, 1), (2, 2, 513, 128, 2), (1, 2, 40, 128, 45), (5, 3, 4097, 128, 7),
+    (1, 12, 16384, 64, 0), (1, 32, 1000, 128, 0), (1, 2, 5000, 64, 64), (1, 1, 20000, 128, 129),
 ])
 def test_decode_shapes(B, H, Tkv, d, splits):
     full_check(Workload(f"decode[{B},{H},{Tkv},d={d},P={splits}]", B, H, 1, Tkv, d, "bf16", False,
                         seed=3 + Tkv, num_splits=splits), api="decode")
-    assert ("combine" in attn.attn_last_kernel()) == (min(splits, Tkv) > 1)
+    used = splits if splits else attn.attn_decode_splits(B, H, H, Tkv, d)
+    assert ("combine" in attn.attn_last_kernel()) == (min(used, Tkv) > 1)
+
+
+def test_decode_batch1_full_size():
+    """One sequence, 12 heads of 64, 16K cached keys: every head, automatic partitions."""
+    full_check(WORKLOADS["decode_b1"], api="decode")
+    assert "combine" in attn.attn_last_kernel()
 
 
 def gqa_check(w: Workload):
@@ -258,11 +266,13 @@ def gqa_check(w: Workload):
     (2, 12, 2, 257, 64, 3),      # groups of 6 (head tile 2)
     (1, 32, 2, 90, 64, 200),     # groups of 16 (two tiles of 8), splits clamped to Tkv
     (1, 4, 1, 1, 128, 16),       # a single cached key
+    (2, 8, 2, 3000, 128, 0),     # automatic partitions
 ])
 def test_gqa_decode_shapes(B, Hq, Hkv, Tkv, d, splits):
     kern = gqa_check(Workload(f"gqa[{B},{Hq}/{Hkv},{Tkv},d={d},P={splits}]", B, Hq, 1, Tkv, d, "bf16", False,
                               seed=40 + Hq + Tkv, num_splits=splits, Hkv=Hkv))
-    assert ("combine" in kern) == (min(splits, Tkv) > 1)
+    used = splits if splits else attn.attn_decode_splits(B, Hq, Hkv, Tkv, d)
+    assert ("combine" in kern) == (min(used, Tkv) > 1)
 
 
 def test_gqa_decode_full_size_sampled():
