@@ -13,6 +13,7 @@ online softmax, causal skipping, the epilogue).  The decode half of the path
 its grouped-query form (the same step with 8 key/value heads for the 32 query
 heads) in "decode_gqa"; "decode_b1" is one sequence (12 heads of 64, 16K
 keys) with automatically chosen partitions against one partition per head.
+"mid_d128" is the mid-length prefill at head width 128.
 "prefill_split" times one 16K-token causal head, a
 shape with too few query tiles to fill the chip, with and without the key
 axis split across workgroups.
@@ -229,6 +230,33 @@ def run_decode(torch, attn, steps, warmup, name="decode"):
     return out
 
 
+def run_prefill(torch, attn, steps, warmup, name):
+    """Another prefill workload, timed like the main one (no oracle leg)."""
+    from io_aware_exact_amd.inputs import WORKLOADS, make_qkv
+
+    w = WORKLOADS[name]
+    q, k, v = make_qkv(w)
+    dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
+    o = torch.empty_like(dq)
+    lse = torch.empty((w.B, w.H, w.Tq), dtype=torch.float32, device="cuda")
+    ms = time_steps(torch, attn.prepared_fwd(dq, dk, dv, o, lse, w.causal, w.scale), steps, warmup)
+    kern = attn.attn_last_kernel()
+    del dq, dk, dv, o, lse
+    torch.cuda.empty_cache()
+    tf = prefill_flops(w) / (ms * 1e-3) / 1e12
+    return {
+        "workload": f"{name} prefill B={w.B} H={w.H} Tq={w.Tq} Tkv={w.Tkv} d={w.d} "
+                    f"{'causal' if w.causal else 'non-causal'} bf16",
+        "metric": "attn fwd TFLOP/s (causal-adjusted)",
+        "value": tf,
+        "unit": "TFLOP/s",
+        "ms_per_step": ms,
+        "kernel": kern,
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / PEAK_BF16_TFLOPS, "traffic": measured_traffic("prefill", name)},
+    }
+
+
 def run_prefill_split(torch, attn, steps, warmup, name="long_1head"):
     """Prefill on a shape with too few query tiles to fill the chip: attn_fwd
     (one workgroup per query tile) against attn_fwd_split (the key axis of
@@ -278,6 +306,7 @@ def main():
     ap.add_argument("--workload", default="gpt2", help="prefill workload: gpt2, mid, mid_causal, long, tiny")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurements")
     ap.add_argument("--no-split", action="store_true", help="skip the split-prefill measurement")
+    ap.add_argument("--no-extra", action="store_true", help="skip the head-width-128 prefill measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle leg: seconds of CPU work")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -360,6 +389,11 @@ def main():
         result["cpu_baseline"] = None
     del dq, dk, dv
     torch.cuda.empty_cache()
+    if not args.no_extra:
+        for name in ("mid_d128",):
+            result[name] = run_prefill(torch, attn, args.steps, args.warmup, name)
+            log(f"[bench] {name} {result[name]['kernel']}: {result[name]['ms_per_step'] * 1e3:.1f} us/step, "
+                f"{result[name]['value']:.1f} TFLOP/s")
     if not args.no_split:
         result["prefill_split"] = run_prefill_split(torch, attn, args.steps, args.warmup)
         log(f"[bench] prefill_split {result['prefill_split']['kernel']}: "

@@ -68,8 +68,9 @@ enum {
  * the output accumulator are fp32 ("IO-Aware Attention", section "Where the
  * approach stops helping": 32-bit accumulation and rescaling); P is rounded to
  * bf16 (nearest even) before the PV product and O is rounded once at the end.
- * Supported: d = 64 for T_q > 1; d in {64, 128} for T_q == 1 (runs the decode
- * kernel unsplit, no workspace).  T_q and T_kv need not be multiples of any tile.
+ * Supported: d in {64, 128} (64- and 32-key blocks); for T_q == 1 the decode
+ * kernel runs unsplit (no workspace).  T_q and T_kv need not be multiples of
+ * any tile.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int Tq, int Tkv, int d, int causal, float scale, hipStream_t stream);

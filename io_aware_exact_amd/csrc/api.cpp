@@ -129,7 +129,7 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
     attn::PrefillArgs a{q, k, v, o, lse, B, H, Tq, Tkv, d, causal != 0, float(double(scale) * kLog2e), ws};
     const char* name = nullptr;
     (void)hipGetLastError();
-    return finish(attn::launch_prefill_bf16_d64(a, split, stream, &name), name);
+    return finish(attn::launch_prefill_bf16(a, split, stream, &name), name);
 }
 
 // Shape checks of the bf16 forward beyond check_common.
@@ -138,16 +138,17 @@ int check_fwd_shape(int B, int H, int Tq, int Tkv, int d) {
         if (d != 64 && d != 128) return fail(ATTN_EUNSUPPORTED, "bf16 single-query path supports d in {64, 128}");
         return ATTN_OK;
     }
-    if (d != 64) return fail(ATTN_EUNSUPPORTED, "bf16 prefill supports d = 64");
-    if (!attn::prefill_bf16_fits(Tkv)) return fail(ATTN_EUNSUPPORTED, "bf16 prefill supports Tkv*d*2 < 2^31 bytes per head");
+    if (!attn::prefill_bf16_supports(d)) return fail(ATTN_EUNSUPPORTED, "bf16 prefill supports d in {64, 128}");
+    if (!attn::prefill_bf16_fits(Tkv, d))
+        return fail(ATTN_EUNSUPPORTED, "bf16 prefill supports Tkv*d*2 < 2^31 bytes per head");
     if (double(B) * H * ((Tq + 127) / 128) > 2147483647.0) return fail(ATTN_EINVAL, "grid too large");
     return ATTN_OK;
 }
 
 // The split plan of attn_fwd_split, or no split when the shape has none.
 attn::PrefillSplit fwd_split_plan(int B, int H, int Tq, int Tkv, int d, int causal, int kv_chunk) {
-    if (Tq == 1 || d != 64) return attn::PrefillSplit{0, 1, 0};
-    attn::PrefillSplit p = attn::prefill_bf16_split_plan(B, H, Tq, Tkv, causal != 0, kv_chunk);
+    if (Tq == 1 || !attn::prefill_bf16_supports(d)) return attn::PrefillSplit{0, 1, 0};
+    attn::PrefillSplit p = attn::prefill_bf16_split_plan(B, H, Tq, Tkv, d, causal != 0, kv_chunk);
     if (double(B) * H * ((Tq + 127) / 128) * p.nch_max > 2147483647.0) return attn::PrefillSplit{0, 1, 0};
     return p;
 }

@@ -20,7 +20,7 @@ struct PrefillArgs {
 };
 
 // How a bf16 prefill is divided into work units: tiles whose key range is
-// longer than `chunk` blocks of 64 keys are split into near-equal chunks.
+// longer than `chunk` key blocks are split into near-equal chunks.
 struct PrefillSplit {
     int chunk;               // blocks per unit (0 = no split)
     int nch_max;             // chunks of the longest tile (1 = no split)
@@ -39,10 +39,11 @@ struct DecodeArgs {
     void* workspace;  // B*H*num_splits*(d+2) floats, unused when num_splits == 1
 };
 
-PrefillSplit prefill_bf16_split_plan(int B, int H, int Tq, int Tkv, bool causal, int kv_chunk);
-hipError_t launch_prefill_bf16_d64(const PrefillArgs& a, const PrefillSplit& split, hipStream_t stream,
-                                   const char** name);
-bool prefill_bf16_fits(int Tkv);
+bool prefill_bf16_supports(int d);
+bool prefill_bf16_fits(int Tkv, int d);
+PrefillSplit prefill_bf16_split_plan(int B, int H, int Tq, int Tkv, int d, bool causal, int kv_chunk);
+hipError_t launch_prefill_bf16(const PrefillArgs& a, const PrefillSplit& split, hipStream_t stream,
+                               const char** name);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream, const char** name);
 bool prefill_f32_supports(int d);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream, const char** name);

@@ -1,7 +1,10 @@
-// Exact attention forward (prefill), bf16 inputs, head width 64, gfx950.
+// Exact attention forward (prefill), bf16 inputs, head width 64 or 128, gfx950.
 //
 // One workgroup owns a tile of BQ = 32 * WAVES query rows of one (batch, head)
-// and streams the key/value blocks of 64 rows past it ("IO-Aware Attention:
+// and streams the key/value blocks of BK rows past it (BK = 64 for d = 64;
+// BK = 32 for d = 128, whose rows are twice as long -- the halved block the
+// head width 128 needs in "IO-Aware Attention", section "What has to stay in
+// fast memory") ("IO-Aware Attention:
 // Tiling the Score Matrix Without Materializing It", section "What has to
 // stay in fast memory"; "FlashAttention IO-aware tiling lab", kernel phases
 // load Q / score a K tile / update the online softmax / accumulate V / write O
@@ -31,11 +34,11 @@
 //   plus one v_permlane32_swap, the softmax rescale is a per-lane scalar, and
 //   the fp32 accumulator of the first product is already the B operand of the
 //   second (only a bf16 pack in between).
-// * Q stays in VGPRs for the whole key loop (16 VGPRs per lane).
+// * Q stays in VGPRs for the whole key loop (d/4 VGPRs per lane).
 // * K and V blocks go from HBM straight into an NS-stage LDS ring with
 //   buffer_load ... lds (no staging registers, no LDS store instructions;
 //   the buffer range check zero-fills the ragged end).  Rows keep their
-//   natural 128-byte layout with the 16-byte chunks XOR-swizzled per row, so
+//   natural 2d-byte layout with the 16-byte chunks XOR-swizzled per row, so
 //   the K operand reads (ds_read_b128) and the V operand reads are free of
 //   bank conflicts.  V is read with ds_read_b64_tr_b16, which hands every
 //   lane four consecutive keys of one column: exactly the operand layout of
@@ -56,20 +59,35 @@
 namespace attn {
 namespace {
 
-constexpr int D = 64;
-constexpr int BK = 64;
-constexpr int ROWB = D * 2;                   // bytes per K/V row
-constexpr int TILEB = BK * ROWB;              // bytes per K (or V) block: 8 KiB
 constexpr float kSumLimit = 65536.0f;         // 2^16: largest block row sum kept without raising m
 
-// 16-byte chunk swizzles (chunk index within a 128-byte row).
-__device__ __forceinline__ int swz_k(int row) { return (row >> 1) & 7; }
-__device__ __forceinline__ int swz_v(int row) { return ((row >> 1) & 1) << 2; }
+// Tile geometry per head width.  Rows are D*2 bytes; LDS chunk swizzles
+// (16-byte chunk index within a row) make the K operand reads (ds_read_b128,
+// 32 rows x one chunk pair per instruction) and the V transposed reads (8
+// rows x 64 bytes per instruction) free of bank conflicts.
+template <int D>
+struct Geo;
+template <>
+struct Geo<64> {
+    static constexpr int BK = 64;
+    // 128-byte rows: two rows share a 256-byte bank line
+    static __device__ __forceinline__ int swz_k(int row) { return (row >> 1) & 7; }
+    static __device__ __forceinline__ int swz_v(int row) { return ((row >> 1) & 1) << 2; }
+};
+template <>
+struct Geo<128> {
+    static constexpr int BK = 32;
+    // 256-byte rows: one row per bank line; K chunks rotate over 16 rows, V's
+    // 64-byte segments over 4
+    static __device__ __forceinline__ int swz_k(int row) { return row & 15; }
+    static __device__ __forceinline__ int swz_v(int row) { return (row & 3) << 2; }
+};
 
-// Key blocks a query tile must visit (causal: up to its last row's diagonal).
-__host__ __device__ __forceinline__ int tile_blocks(int qt, int bq, int Tq, int Tkv, bool causal) {
+// Key blocks of bk keys a query tile must visit (causal: up to its last
+// row's diagonal).
+__host__ __device__ __forceinline__ int tile_blocks(int qt, int bq, int bk, int Tq, int Tkv, bool causal) {
     const int kend = causal ? min(Tkv, (qt + 1) * bq + (Tkv - Tq)) : Tkv;
-    return (kend + BK - 1) / BK;
+    return (kend + bk - 1) / bk;
 }
 
 // Chunks a tile of nblk key blocks is split into when a work unit takes at
@@ -83,15 +101,25 @@ __host__ __device__ __forceinline__ int tile_chunks(int nblk, int chunk) {
 // Units of unsplit tiles write O and LSE; units of split tiles write their
 // partial result (O normalised by the chunk's own sum, and the chunk's
 // base-2 log-sum-exp) to `part`, merged later by prefill_combine_kernel.
-template <int WAVES, int NS, bool CAUSAL>
+template <int D, int WAVES, int NS, bool CAUSAL>
 __global__ __launch_bounds__(WAVES * 64, 2)
-void prefill_bf16_d64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                             const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                             float* __restrict__ LSE, float* __restrict__ part, int Tq, int Tkv, int BH,
-                             int nqt, int chunk, int nch_max, float c) {
+void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                         const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+                         float* __restrict__ LSE, float* __restrict__ part, int Tq, int Tkv, int BH,
+                         int nqt, int chunk, int nch_max, float c) {
+    using G = Geo<D>;
+    constexpr int BK = G::BK;
     constexpr int BQ = WAVES * 32;
-    static_assert(8 % WAVES == 0, "row groups of a block must split evenly over the waves");
-    constexpr int LI = 8 / WAVES;             // 1 KiB load instructions per wave per operand per block
+    constexpr int ROWB = D * 2;               // bytes per K/V row
+    constexpr int TILEB = BK * ROWB;          // bytes per K (or V) block: 8 KiB
+    constexpr int CPR = ROWB / 16;            // 16-byte chunks per row
+    constexpr int RPG = 1024 / ROWB;          // rows per 1 KiB load instruction
+    constexpr int TQ = D / 16;                // k-steps of the QK product
+    constexpr int DT = D / 32;                // 32-column tiles of O
+    constexpr int KT = BK / 32;               // 32-key tiles of S
+    constexpr int ST = BK / 16;               // 16-key steps of the PV product
+    static_assert((TILEB / 1024) % WAVES == 0, "row groups of a block must split evenly over the waves");
+    constexpr int LI = TILEB / 1024 / WAVES;  // 1 KiB load instructions per wave per operand per block
 
     __shared__ __attribute__((aligned(1024))) uint8_t ring[NS][2][TILEB];
 
@@ -113,7 +141,7 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __r
     const int q0 = qt * BQ;
     const int off = Tkv - Tq;                 // bottom-right causal alignment
 
-    const int nblk = tile_blocks(qt, BQ, Tq, Tkv, CAUSAL);
+    const int nblk = tile_blocks(qt, BQ, BK, Tq, Tkv, CAUSAL);
     const int nch = tile_chunks(nblk, chunk);
     if (cc >= nch) return;                    // this tile has fewer chunks (uniform per workgroup)
     const int jlo = (int)(((long long)cc * nblk) / nch);
@@ -126,29 +154,29 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __r
 
     // ---- Q fragment: row q0 + 32*wave + ln, d = 16t + 8hf + (0..7) ----
     const int qrow = q0 + wave * 32 + ln;
-    bf16x8_t qf[4];
+    bf16x8_t qf[TQ];
     if (qrow < Tq) {
         const u32x4_t* src = reinterpret_cast<const u32x4_t*>(Q + qbase + (size_t)qrow * D + 8 * hf);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) qf[t] = __builtin_bit_cast(bf16x8_t, src[2 * t]);
+        for (int t = 0; t < TQ; ++t) qf[t] = __builtin_bit_cast(bf16x8_t, src[2 * t]);
     } else {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) qf[t] = __builtin_bit_cast(bf16x8_t, u32x4_t{0, 0, 0, 0});
+        for (int t = 0; t < TQ; ++t) qf[t] = __builtin_bit_cast(bf16x8_t, u32x4_t{0, 0, 0, 0});
     }
 
     const int wq_first = q0 + wave * 32;       // this wave's first / last query row
     const int wq_last = wq_first + 31;
     const int lim = CAUSAL ? min(Tkv - 1, qrow + off) : (Tkv - 1);   // last key this row may see
 
-    // ---- DMA loads: wave w moves row groups g = w + WAVES*i (8 rows = 1 KiB each) ----
+    // ---- DMA loads: wave w moves row groups g = w + WAVES*i (RPG rows = 1 KiB each) ----
     uint32_t k_voff[LI], v_voff[LI];
 #pragma unroll
     for (int i = 0; i < LI; ++i) {
         const int g = wave + WAVES * i;
-        const int row = 8 * g + (lane >> 3);
-        const int slot = lane & 7;            // the chunk position this lane fills in LDS
-        k_voff[i] = (uint32_t)(row * ROWB + ((slot ^ swz_k(row)) << 4));
-        v_voff[i] = (uint32_t)(row * ROWB + ((slot ^ swz_v(row)) << 4));
+        const int row = RPG * g + lane / CPR;
+        const int slot = lane % CPR;          // the chunk position this lane fills in LDS
+        k_voff[i] = (uint32_t)(row * ROWB + ((slot ^ G::swz_k(row)) << 4));
+        v_voff[i] = (uint32_t)(row * ROWB + ((slot ^ G::swz_v(row)) << 4));
     }
     // Block j goes to stage j % NS.  Blocks past the unit's end still issue
     // (empty range, no memory traffic) so that every wave's vmcnt stays uniform.
@@ -169,27 +197,27 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __r
     };
 
     // ---- per-lane LDS read offsets (within a stage) ----
-    // K operand of step t: row 32kt + ln, chunk 2t + hf (kt adds 32 rows = 4 KiB).
-    uint32_t k_roff[4];
+    // K operand of step t: row 32kt + ln, chunk 2t + hf (kt adds 32 rows).
+    uint32_t k_roff[TQ];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) k_roff[t] = (uint32_t)(ln * ROWB + (((2 * t + hf) ^ swz_k(ln)) << 4));
-    // V operand (transposed read) of step st, d-tile dt: lane group G = lane / 16,
-    // j = lane % 16 addresses row 16st + 4(G/2) + j/4 (+8 for the second half),
-    // columns 32dt + 16(G%2) + 4(j%4) .. +3 (st adds 2 KiB).
-    uint32_t v_roff[2];
+    for (int t = 0; t < TQ; ++t) k_roff[t] = (uint32_t)(ln * ROWB + (((2 * t + hf) ^ G::swz_k(ln)) << 4));
+    // V operand (transposed read) of step st, d-tile dt: lane group lg = lane / 16,
+    // j = lane % 16 addresses row 16st + 4(lg/2) + j/4 (+8 for the second half),
+    // columns 32dt + 16(lg%2) + 4(j%4) .. +3 (st adds 16 rows).
+    uint32_t v_roff[DT];
     {
-        const int G = lane >> 4, jj = lane & 15;
-        const int row = 4 * (G >> 1) + (jj >> 2);
+        const int lg = lane >> 4, jj = lane & 15;
+        const int row = 4 * (lg >> 1) + (jj >> 2);
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-            const int col = 32 * dt + 16 * (G & 1) + 4 * (jj & 3);
-            v_roff[dt] = (uint32_t)(row * ROWB + ((((col >> 3) ^ swz_v(row)) << 4) | ((col & 4) << 1)));
+        for (int dt = 0; dt < DT; ++dt) {
+            const int col = 32 * dt + 16 * (lg & 1) + 4 * (jj & 3);
+            v_roff[dt] = (uint32_t)(row * ROWB + ((((col >> 3) ^ G::swz_v(row)) << 4) | ((col & 4) << 1)));
         }
     }
 
-    f32x16_t oacc[2];
+    f32x16_t oacc[DT];
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
     float m = kNegInf;   // reference max of S * c (log2 units), raised only when needed
@@ -199,20 +227,20 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __r
     auto step = [&](const uint8_t* kst, int kb, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const uint8_t* vst = kst + TILEB;
-        f32x16_t s[2];
+        f32x16_t s[KT];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
+            for (int t = 0; t < TQ; ++t) {
                 const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kst + k_roff[t] + kt * 32 * ROWB);
                 s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kt], 0, 0, 0);
             }
         }
         if constexpr (MASK) {
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = kb + 32 * kt + 8 * (r >> 2) + 4 * hf + (r & 3);
@@ -220,12 +248,12 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __r
                 }
         }
         // exponentials against the current reference; packed to bf16 pairs
-        uint32_t pw[16];
+        uint32_t pw[8 * KT];
         float rs = 0.f;
         auto exponentiate = [&](float mref) {
             rs = 0.f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
+            for (int i = 0; i < 8 * KT; ++i) {
                 const int kt = i >> 3, r = 2 * (i & 7);
                 const float p0 = fast_exp2(__builtin_fmaf(s[kt][r], c, -mref));
                 const float p1 = fast_exp2(__builtin_fmaf(s[kt][r + 1], c, -mref));
@@ -239,7 +267,7 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __r
             // raise the reference to the true running max and rescale
             float mx = kNegInf;
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
             mx = half_swap_max(mx);
@@ -248,34 +276,40 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __r
             const float alpha = fast_exp2(m - m_use);
             l *= alpha;
 #pragma unroll
-            for (int dt = 0; dt < 2; ++dt)
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
             m = m_new;
             exponentiate(m_use);
         }
         l += rs;
-        const uint32_t va0 = lds_addr(vst) + v_roff[0];
-        const uint32_t va1 = lds_addr(vst) + v_roff[1];
+        const uint32_t vbase = lds_addr(vst);
         auto pv_step = [&](auto st_tag) {
             constexpr int st = decltype(st_tag)::value;
             constexpr int o = st * 16 * ROWB;
-            u32x2_t lo0 = lds_read_tr16_b64<o>(va0);
-            u32x2_t hi0 = lds_read_tr16_b64<o + 8 * ROWB>(va0);
-            u32x2_t lo1 = lds_read_tr16_b64<o>(va1);
-            u32x2_t hi1 = lds_read_tr16_b64<o + 8 * ROWB>(va1);
-            lgkm_wait_4(lo0, hi0, lo1, hi1);
             const u32x4_t pv = {pw[4 * st], pw[4 * st + 1], pw[4 * st + 2], pw[4 * st + 3]};
             const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pv);
-            const u32x4_t a0 = {lo0[0], lo0[1], hi0[0], hi0[1]};
-            const u32x4_t a1 = {lo1[0], lo1[1], hi1[0], hi1[1]};
-            oacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a0), pb, oacc[0], 0, 0, 0);
-            oacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a1), pb, oacc[1], 0, 0, 0);
+#pragma unroll
+            for (int d2 = 0; d2 < DT; d2 += 2) {
+                u32x2_t lo0 = lds_read_tr16_b64<o>(vbase + v_roff[d2]);
+                u32x2_t hi0 = lds_read_tr16_b64<o + 8 * ROWB>(vbase + v_roff[d2]);
+                u32x2_t lo1 = lds_read_tr16_b64<o>(vbase + v_roff[d2 + 1]);
+                u32x2_t hi1 = lds_read_tr16_b64<o + 8 * ROWB>(vbase + v_roff[d2 + 1]);
+                lgkm_wait_4(lo0, hi0, lo1, hi1);
+                const u32x4_t a0 = {lo0[0], lo0[1], hi0[0], hi0[1]};
+                const u32x4_t a1 = {lo1[0], lo1[1], hi1[0], hi1[1]};
+                oacc[d2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a0), pb, oacc[d2],
+                                                                   0, 0, 0);
+                oacc[d2 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a1), pb,
+                                                                       oacc[d2 + 1], 0, 0, 0);
+            }
         };
         pv_step(std::integral_constant<int, 0>{});
         pv_step(std::integral_constant<int, 1>{});
-        pv_step(std::integral_constant<int, 2>{});
-        pv_step(std::integral_constant<int, 3>{});
+        if constexpr (ST > 2) {
+            pv_step(std::integral_constant<int, 2>{});
+            pv_step(std::integral_constant<int, 3>{});
+        }
     };
 
     // Blocks [0, nfull) need no element mask for any row of the tile: they lie
@@ -314,7 +348,7 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __r
             float* prow = part + (rec * BQ + (qrow - q0)) * D;
             const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
 #pragma unroll
-            for (int dt = 0; dt < 2; ++dt)
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     float4 w;
@@ -335,7 +369,7 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __r
         const float inv = 1.0f / lsum;
         uint16_t* orow = O + qbase + (size_t)qrow * D;
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const u32x2_t w = {pack_bf16x2(oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv),
@@ -353,20 +387,22 @@ void prefill_bf16_d64_kernel(const uint16_t* __restrict__ Q, const uint16_t* __r
 // rescaling merge of "IO-Aware Attention", section "Parallelism and the cost
 // of the split", applied online over groups of CG chunks so that every load
 // of a group is in flight at once.  blockIdx.x = tile (qt * BH + bh, the XCD
-// of the tile's units), blockIdx.y = a slice of 16 rows; each thread owns 4
-// columns of one row.
+// of the tile's units), blockIdx.y = a slice of 256 / (D/4) rows; each thread
+// owns 4 columns of one row.
 constexpr int CG = 4;
 
-template <int BQ>
+template <int D, int BQ>
 __global__ __launch_bounds__(256)
 void prefill_combine_kernel(const float* __restrict__ part, uint16_t* __restrict__ O, float* __restrict__ LSE,
                             int Tq, int Tkv, int BH, int nqt, int chunk, int nch_max, int causal) {
+    constexpr int TPR = D / 4;                // threads per row
+    constexpr int RPW = 256 / TPR;            // rows per workgroup
     const int bh = blockIdx.x % BH;
     const int qt = blockIdx.x / BH;
-    const int nch = tile_chunks(tile_blocks(qt, BQ, Tq, Tkv, causal != 0), chunk);
+    const int nch = tile_chunks(tile_blocks(qt, BQ, Geo<D>::BK, Tq, Tkv, causal != 0), chunk);
     if (nch <= 1) return;
-    const int r = blockIdx.y * 16 + (threadIdx.x >> 4);
-    const int col = 4 * (threadIdx.x & 15);
+    const int r = blockIdx.y * RPW + (int)threadIdx.x / TPR;
+    const int col = 4 * ((int)threadIdx.x % TPR);
     const int qrow = qt * BQ + r;
     if (qrow >= Tq) return;
     const size_t rec0 = ((size_t)bh * nqt + qt) * nch_max;
@@ -412,79 +448,92 @@ constexpr int kWaves = 4;
 constexpr int kStages = 3;
 constexpr int kBQ = kWaves * 32;
 
-template <bool CAUSAL>
+template <int D, bool CAUSAL>
 hipError_t launch_one(const PrefillArgs& a, int chunk, int nch_max, hipStream_t stream) {
     const int nqt = (a.Tq + kBQ - 1) / kBQ;
     const long long tiles = (long long)nqt * a.B * a.H;
     const long long grid = tiles * nch_max;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((prefill_bf16_d64_kernel<kWaves, kStages, CAUSAL>), dim3((unsigned)grid), dim3(kWaves * 64),
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, kWaves, kStages, CAUSAL>), dim3((unsigned)grid), dim3(kWaves * 64),
                        0, stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
                        static_cast<float*>(a.workspace), a.Tq, a.Tkv, a.B * a.H, nqt, chunk, nch_max, a.c);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nch_max <= 1) return e;
-    hipLaunchKernelGGL((prefill_combine_kernel<kBQ>), dim3((unsigned)tiles, kBQ / 16), dim3(256), 0, stream,
+    constexpr int RPW = 256 / (D / 4);
+    hipLaunchKernelGGL((prefill_combine_kernel<D, kBQ>), dim3((unsigned)tiles, kBQ / RPW), dim3(256), 0, stream,
                        static_cast<const float*>(a.workspace), static_cast<uint16_t*>(a.o), a.lse, a.Tq, a.Tkv,
                        a.B * a.H, nqt, chunk, nch_max, a.causal ? 1 : 0);
     return hipGetLastError();
 }
 
+int block_keys(int d) { return d == 128 ? Geo<128>::BK : Geo<64>::BK; }
+
 thread_local char g_name[128];
 
 }  // namespace
 
-bool prefill_bf16_fits(int Tkv) {
+bool prefill_bf16_supports(int d) { return d == 64 || d == 128; }
+
+bool prefill_bf16_fits(int Tkv, int d) {
     // buffer-load ranges are 32-bit byte counts per (batch, head)
-    return (long long)Tkv * D * 2 < (1LL << 31);
+    return (long long)Tkv * d * 2 < (1LL << 31);
 }
 
-PrefillSplit prefill_bf16_split_plan(int B, int H, int Tq, int Tkv, bool causal, int kv_chunk) {
+PrefillSplit prefill_bf16_split_plan(int B, int H, int Tq, int Tkv, int d, bool causal, int kv_chunk) {
     PrefillSplit p{0, 1, 0};
+    if (!prefill_bf16_supports(d)) return p;
+    const int bk = block_keys(d);
     const int nqt = (Tq + kBQ - 1) / kBQ;
     int maxb = 0;
     long long total = 0;
     for (int qt = 0; qt < nqt; ++qt) {
-        const int nb = tile_blocks(qt, kBQ, Tq, Tkv, causal);
+        const int nb = tile_blocks(qt, kBQ, bk, Tq, Tkv, causal);
         maxb = nb > maxb ? nb : maxb;
         total += nb;
     }
     int chunk = 0;
     if (kv_chunk > 0) {
-        chunk = (kv_chunk + BK - 1) / BK;
+        chunk = (kv_chunk + bk - 1) / bk;
     } else {
         // automatic: split only when the query tiles alone leave the chip
         // short of work (fewer than 3 resident tiles per compute unit), with
         // units of an even share of all key blocks over 768 slots but never
-        // under 16 blocks -- a unit pays a few microseconds of start-up
+        // under 1024 keys -- a unit pays a few microseconds of start-up
         // latency plus its partial's round trip, which shorter units do not
         // earn back (measured on 1-16 heads of 1K-16K keys).
         const long long slots = 3LL * 256;
         const long long tiles = (long long)nqt * B * H;
         if (tiles < slots) {
             const long long share = (total * B * H + slots - 1) / slots;
-            chunk = (int)(share < 16 ? 16 : share);
+            const int min_blocks = 1024 / bk;
+            chunk = (int)(share < min_blocks ? min_blocks : share);
         }
     }
     if (chunk <= 0 || chunk >= maxb) return p;
     p.chunk = chunk;
     p.nch_max = tile_chunks(maxb, chunk);
-    p.workspace_bytes = (size_t)B * H * nqt * p.nch_max * kBQ * (D + 1) * sizeof(float);
+    p.workspace_bytes = (size_t)B * H * nqt * p.nch_max * kBQ * (d + 1) * sizeof(float);
     return p;
 }
 
-hipError_t launch_prefill_bf16_d64(const PrefillArgs& a, const PrefillSplit& sp, hipStream_t stream,
-                                   const char** name) {
+hipError_t launch_prefill_bf16(const PrefillArgs& a, const PrefillSplit& sp, hipStream_t stream,
+                               const char** name) {
+    const int bk = block_keys(a.d);
     if (sp.nch_max > 1)
-        snprintf(g_name, sizeof g_name, "prefill_bf16_d64<waves=4,bq=128,bk=64,stages=3%s,kv_chunk=%d>+combine",
-                 a.causal ? ",causal" : "", sp.chunk * BK);
+        snprintf(g_name, sizeof g_name, "prefill_bf16_d%d<waves=4,bq=128,bk=%d,stages=3%s,kv_chunk=%d>+combine",
+                 a.d, bk, a.causal ? ",causal" : "", sp.chunk * bk);
     else
-        snprintf(g_name, sizeof g_name, "prefill_bf16_d64<waves=4,bq=128,bk=64,stages=3%s>",
+        snprintf(g_name, sizeof g_name, "prefill_bf16_d%d<waves=4,bq=128,bk=%d,stages=3%s>", a.d, bk,
                  a.causal ? ",causal" : "");
     *name = g_name;
     const int chunk = sp.nch_max > 1 ? sp.chunk : 0;
-    if (a.causal) return launch_one<true>(a, chunk, sp.nch_max, stream);
-    return launch_one<false>(a, chunk, sp.nch_max, stream);
+    if (a.d == 128) {
+        if (a.causal) return launch_one<128, true>(a, chunk, sp.nch_max, stream);
+        return launch_one<128, false>(a, chunk, sp.nch_max, stream);
+    }
+    if (a.causal) return launch_one<64, true>(a, chunk, sp.nch_max, stream);
+    return launch_one<64, false>(a, chunk, sp.nch_max, stream);
 }
 
 }  // namespace attn

@@ -69,6 +69,9 @@ WORKLOADS = {
     # mid-length prefill, K rows scaled by 3 to spread the scores
     "mid": Workload("mid", 2, 16, 4096, 4096, 64, "bf16", False, seed=3, k_factor=3.0),
     "mid_causal": Workload("mid_causal", 2, 16, 4096, 4096, 64, "bf16", True, seed=3, k_factor=3.0),
+    # the mid-length prefill at head width 128
+    "mid_d128": Workload("mid_d128", 2, 16, 4096, 4096, 128, "bf16", False, seed=10, k_factor=3.0),
+    "mid_d128_causal": Workload("mid_d128_causal", 2, 16, 4096, 4096, 128, "bf16", True, seed=10, k_factor=3.0),
     # long-context causal prefill
     "long": Workload("long", 1, 12, 16384, 16384, 64, "bf16", True, seed=4),
     # one head of a 16K-token sequence (batch 1): too few query tiles to fill

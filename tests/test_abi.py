@@ -101,7 +101,8 @@ def test_invalid_arguments(lib, call, bad, want):
 
 
 def test_unsupported_head_widths(lib):
-    assert fwd(lib, d=128) == EUNSUP and "d = 64" in attn.attn_status_string(EUNSUP)
+    assert fwd(lib, d=96) == EUNSUP and "{64, 128}" in attn.attn_status_string(EUNSUP)
+    assert fwd(lib, d=32) == EUNSUP
     assert fwd(lib, d=96, Tq=1) == EUNSUP
     assert fwd32(lib, d=96) == EUNSUP
     assert fwd32(lib, d=256) == EUNSUP
@@ -144,7 +145,7 @@ def test_split_forward_arguments(lib):
     assert fsplit(lib, wsb=need - 1) == EWS and str(need) in attn.attn_status_string(EWS)
     assert fsplit(lib, ws=W + 8) == EINVAL and "aligned" in attn.attn_status_string(EINVAL)
     assert fsplit(lib, ws=V + 4096) == EINVAL and "overlaps" in attn.attn_status_string(EINVAL)
-    assert fsplit(lib, d=128) == EUNSUP
+    assert fsplit(lib, d=96) == EUNSUP
 
 
 def test_split_forward_workspace_formula():
@@ -165,7 +166,9 @@ def test_split_forward_workspace_formula():
     assert attn.attn_fwd_split_workspace_bytes(1, 2, 8192, 8192, 64, True, 0) == 2 * 64 * 8 * per_unit
     # invalid or unsupported -> 0
     assert attn.attn_fwd_split_workspace_bytes(4, 12, 1024, 1024, 64, True, -1) == 0
-    assert attn.attn_fwd_split_workspace_bytes(4, 12, 1024, 1024, 128, True, 256) == 0
+    assert attn.attn_fwd_split_workspace_bytes(4, 12, 1024, 1024, 96, True, 256) == 0
+    # d = 128 uses 32-key blocks: 1024 keys -> 32 blocks, units of 256 keys -> 4 chunks
+    assert attn.attn_fwd_split_workspace_bytes(4, 12, 1024, 1024, 128, True, 256) == 4 * 12 * 8 * 4 * 128 * 129 * 4
     assert attn.attn_fwd_split_workspace_bytes(4, 12, 1, 1024, 64, False, 256) == 0
     assert attn.attn_fwd_split_workspace_bytes(4, 12, 2048, 1024, 64, True, 256) == 0
 

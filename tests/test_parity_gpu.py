@@ -83,7 +83,7 @@ def _sampled_rows(T, n, rng):
     return np.array(sorted(set(r for r in edge + rnd if 0 <= r < T)))
 
 
-@pytest.mark.parametrize("name", ["mid", "mid_causal", "long"])
+@pytest.mark.parametrize("name", ["mid", "mid_causal", "long", "mid_d128", "mid_d128_causal"])
 def test_prefill_full_size_sampled(name):
     w = WORKLOADS[name]
     say(f"case {w} (sampled rows)")
@@ -141,10 +141,13 @@ PREFILL_CASES = [
 ]
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("B,H,Tq,Tkv,causal", PREFILL_CASES)
-def test_prefill_bf16_shapes(B, H, Tq, Tkv, causal):
-    full_check(Workload(f"bf16[{B},{H},{Tq},{Tkv},{'c' if causal else 'n'}]", B, H, Tq, Tkv, 64, "bf16", causal,
-                        seed=11 + Tq + Tkv))
+def test_prefill_bf16_shapes(B, H, Tq, Tkv, causal, d):
+    full_check(Workload(f"bf16[{B},{H},{Tq},{Tkv},{'c' if causal else 'n'},d={d}]", B, H, Tq, Tkv, d, "bf16",
+                        causal, seed=11 + Tq + Tkv + d))
+    if Tq > 1:
+        assert attn.attn_last_kernel().startswith(f"prefill_bf16_d{d}<")
 
 
 @pytest.mark.parametrize("d", [16, 32, 64, 128])
@@ -169,10 +172,11 @@ SPLIT_CASES = [
 ]
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("B,H,Tq,Tkv,causal,chunk", SPLIT_CASES)
-def test_prefill_split_shapes(B, H, Tq, Tkv, causal, chunk):
-    w = Workload(f"split[{B},{H},{Tq},{Tkv},{'c' if causal else 'n'},kv={chunk}]", B, H, Tq, Tkv, 64, "bf16",
-                 causal, seed=60 + Tq + Tkv)
+def test_prefill_split_shapes(B, H, Tq, Tkv, causal, chunk, d):
+    w = Workload(f"split[{B},{H},{Tq},{Tkv},{'c' if causal else 'n'},kv={chunk},d={d}]", B, H, Tq, Tkv, d, "bf16",
+                 causal, seed=60 + Tq + Tkv + d)
     say(f"case {w}")
     q, k, v = make_qkv(w)
     dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
@@ -180,7 +184,7 @@ def test_prefill_split_shapes(B, H, Tq, Tkv, causal, chunk):
     torch.cuda.synchronize()
     kern = attn.attn_last_kernel()
     say(f"  kernel {kern}")
-    split = attn.attn_fwd_split_workspace_bytes(B, H, Tq, Tkv, 64, causal, chunk) > 0
+    split = attn.attn_fwd_split_workspace_bytes(B, H, Tq, Tkv, d, causal, chunk) > 0
     assert ("combine" in kern) == split
     o_ref, lse_ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), w.scale, causal)
     compare(w, o, lse, o_ref, lse_ref)
