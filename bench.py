@@ -294,7 +294,7 @@ def run_prefill_split(torch, attn, steps, warmup, name="long_1head"):
         "speedup_vs_unsplit": ms_plain / ms,
         "max_abs_diff_vs_unsplit_o": diff,
         "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tf / PEAK_BF16_TFLOPS, "traffic": None},
+                     "frac": tf / PEAK_BF16_TFLOPS, "traffic": measured_traffic("prefill_split", name)},
     }
 
 
