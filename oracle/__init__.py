@@ -14,6 +14,9 @@ forward computes, written from the source pages:
   (partial outputs over key partitions merged with the same rescaling).
 * "E8.1 IO-aware attention" (coursefy.online), the worked example and the
   "Do it in code" function specs.
+* Backward (``backward.py``): "IO-Aware Attention", section "What has to stay
+  in fast memory" -- P is recomputed from Q, K, V and the saved row constants;
+  the gradient formulas are the calculus of the forward definition.
 
 Who may use it: only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py``.  The product package
@@ -21,8 +24,8 @@ Who may use it: only ``tests/``, ``__graft_entry__.smoke()`` and the
 nothing here imports the product package.  The oracle shares no code, tables
 or constants with the HIP path.
 
-Parity status: every public function is pinned by ``tests/test_oracle.py``
-and ``tests/test_cost_model.py`` against values printed on the pages
+Parity status: every public function is pinned by ``tests/test_oracle.py``,
+``tests/test_oracle_backward.py`` and ``tests/test_cost_model.py`` against values printed on the pages
 (``tests/golden/``), closed forms, special cases, brute force on tiny inputs
 and a library routine; none is "parity unpinned".
 """
@@ -36,6 +39,7 @@ from .attention import (
     split_attention,
     standard_attention,
 )
+from .backward import attention_backward, attention_backward_from_lse
 from .cost import (
     attention_flops,
     causal_pairs,
@@ -50,6 +54,8 @@ from .cost import (
 
 __all__ = [
     "attention",
+    "attention_backward",
+    "attention_backward_from_lse",
     "attention_gqa",
     "combine_partials",
     "online_attention",
