@@ -13,7 +13,8 @@ online softmax, causal skipping, the epilogue).  The decode half of the path
 its grouped-query form (the same step with 8 key/value heads for the 32 query
 heads) in "decode_gqa"; "decode_b1" is one sequence (12 heads of 64, 16K
 keys) with automatically chosen partitions against one partition per head.
-"mid_d128" is the mid-length prefill at head width 128.
+"mid_d128" is the mid-length prefill at head width 128; "backward" is the
+backward pass (attn_bwd) on the GPT-2-shaped workload.
 "prefill_split" times one 16K-token causal head, a
 shape with too few query tiles to fill the chip, with and without the key
 axis split across workgroups.
@@ -257,6 +258,51 @@ def run_prefill(torch, attn, steps, warmup, name):
     }
 
 
+def run_backward(torch, attn, steps, warmup, name="gpt2"):
+    """The backward pass (attn_bwd) on a prefill workload: forward once for O
+    and LSE, then time the three backward kernels; parity of dV on sampled
+    heads against the float64 backward oracle."""
+    import numpy as np
+
+    import oracle
+    from io_aware_exact_amd.inputs import WORKLOADS, make_qkv, make_tensor, to_f64
+
+    w = WORKLOADS[name]
+    q, k, v = make_qkv(w)
+    do = make_tensor(w.seed + 1000, "v", w.B, w.H, w.Tq, w.d, "bf16")
+    dq_, dk_, dv_, ddo = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = attn.attn_fwd(dq_, dk_, dv_, causal=w.causal, scale=w.scale)
+    gq = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    gk = torch.empty(k.shape, dtype=torch.float32, device="cuda")
+    gv = torch.empty(v.shape, dtype=torch.float32, device="cuda")
+    ws = torch.empty(attn.attn_bwd_workspace_bytes(w.B, w.H, w.Tq), dtype=torch.uint8, device="cuda")
+    call = attn.prepared_bwd(dq_, dk_, dv_, o, lse, ddo, gq, gk, gv, w.causal, ws, w.scale)
+    ms = time_steps(torch, call, steps, warmup)
+    kern = attn.attn_last_kernel()
+    errs = []
+    for b, h in [(0, 0), (w.B - 1, w.H - 1), (w.B // 2, w.H // 3)]:
+        rq, rk, rv, _ = oracle.attention_backward(to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]),
+                                                  to_f64(do[b, h]), w.scale, w.causal)
+        errs.append(max(float(np.abs(to_f64(g[b, h]) - r).max()) for g, r in ((gq, rq), (gk, rk), (gv, rv))))
+    del dq_, dk_, dv_, ddo, o, lse, gq, gk, gv, ws
+    torch.cuda.empty_cache()
+    # model flops: the 5 products of the standard backward (S, dP, dV, dK, dQ), 2 d flops per pair each
+    flops = 5 * 2 * w.B * w.H * w.d * visible_pairs(w.Tq, w.Tkv, w.causal)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {
+        "workload": f"{name} backward B={w.B} H={w.H} Tq={w.Tq} Tkv={w.Tkv} d={w.d} "
+                    f"{'causal' if w.causal else 'non-causal'} bf16 in, fp32 dQ/dK/dV",
+        "metric": "attn bwd TFLOP/s (5 products, causal-adjusted)",
+        "value": tf,
+        "unit": "TFLOP/s",
+        "ms_per_step": ms,
+        "kernel": kern,
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / PEAK_BF16_TFLOPS, "traffic": measured_traffic("backward", name)},
+        "parity": {"max_abs_err_dq_dk_dv": max(errs), "heads_checked": len(errs)},
+    }
+
+
 def run_prefill_split(torch, attn, steps, warmup, name="long_1head"):
     """Prefill on a shape with too few query tiles to fill the chip: attn_fwd
     (one workgroup per query tile) against attn_fwd_split (the key axis of
@@ -307,6 +353,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurements")
     ap.add_argument("--no-split", action="store_true", help="skip the split-prefill measurement")
     ap.add_argument("--no-extra", action="store_true", help="skip the head-width-128 prefill measurement")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle leg: seconds of CPU work")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -394,6 +441,10 @@ def main():
             result[name] = run_prefill(torch, attn, args.steps, args.warmup, name)
             log(f"[bench] {name} {result[name]['kernel']}: {result[name]['ms_per_step'] * 1e3:.1f} us/step, "
                 f"{result[name]['value']:.1f} TFLOP/s")
+    if not args.no_backward:
+        result["backward"] = run_backward(torch, attn, args.steps, args.warmup)
+        log(f"[bench] backward {result['backward']['kernel']}: {result['backward']['ms_per_step'] * 1e3:.1f} us/step, "
+            f"{result['backward']['value']:.1f} TFLOP/s")
     if not args.no_split:
         result["prefill_split"] = run_prefill_split(torch, attn, args.steps, args.warmup)
         log(f"[bench] prefill_split {result['prefill_split']['kernel']}: "

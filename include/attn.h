@@ -179,6 +179,43 @@ int attn_decode_gqa(const void* q, const void* k, const void* v, void* o, float*
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * attn_bwd_workspace_bytes -- bytes of workspace attn_bwd needs: B*H*Tq*8
+ * (per query row its log-sum-exp in base 2 and D = sum_d dO*O, fp32).
+ * 0 when any size is < 1.
+ */
+size_t attn_bwd_workspace_bytes(int B, int H, int Tq);
+
+/*
+ * attn_bwd -- backward pass of attn_fwd: gradients of sum(O * dO) with
+ * respect to Q, K and V, recomputing the softmax from Q, K, V and the saved
+ * per-row log-sum-exp instead of storing it ("IO-Aware Attention", section
+ * "What has to stay in fast memory": the saved state is O(n d) plus O(n) row
+ * constants).  With P = exp(scale*Q K^T - lse) (masked entries 0) and
+ * D_i = sum_d dO_id O_id:
+ *
+ *     dV = P^T dO,  dS = P * (dO V^T - D),  dQ = scale dS K,  dK = scale dS^T Q
+ *
+ *   q, k, v    the forward's bf16 inputs [B,H,Tq,d], [B,H,Tkv,d] (x2)
+ *   o, lse     the forward's bf16 output [B,H,Tq,d] and fp32 LSE [B,H,Tq]
+ *              (natural log, as attn_fwd writes it; required)
+ *   dout       bf16 upstream gradient dO [B,H,Tq,d]
+ *   dq, dk, dv fp32 outputs [B,H,Tq,d], [B,H,Tkv,d] (x2), fully written
+ *   causal, scale   as in the forward call
+ *   workspace  at least attn_bwd_workspace_bytes(B,H,Tq) bytes; contents on
+ *              entry are ignored
+ *
+ * Three kernels on `stream` (row statistics, dK/dV per key tile, dQ per query
+ * tile); no atomics, so results are deterministic.  Products are bf16 MFMA with
+ * fp32 accumulation; P and dS are rounded to bf16 as MFMA operands.
+ * Errors: as attn_fwd, plus ATTN_EINVAL for NULL dout/lse/dq/dk/dv or
+ * overlapping buffers, ATTN_EWORKSPACE for a missing or small workspace.
+ * Supported: d = 64.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+             float* dq, float* dk, float* dv, int B, int H, int Tq, int Tkv, int d, int causal, float scale,
+             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * attn_last_kernel -- name and tile configuration of the kernel(s) enqueued by
  * this thread's last successful call, e.g.
  * "prefill_bf16_d64<waves=4,bq=128,bk=64,causal>" ("Attention and Its

@@ -35,6 +35,8 @@ SIGNATURES = {
     "attn_decode_splits": (_I, [_I, _I, _I, _I, _I]),
     "attn_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _S, _P]),
     "attn_decode_gqa": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _S, _P]),
+    "attn_bwd_workspace_bytes": (_S, [_I, _I, _I]),
+    "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _S, _P]),
     "attn_last_kernel": (ctypes.c_char_p, []),
     "attn_status_string": (ctypes.c_char_p, [_I]),
 }
@@ -234,6 +236,49 @@ def attn_decode_gqa(q, k, v, scale: float | None = None, num_splits: int = 16, w
                                scale, int(num_splits), wp, wbytes, _stream())
     _check(st)
     return (o, lse) if return_lse else o
+
+
+def attn_bwd_workspace_bytes(B: int, H: int, Tq: int) -> int:
+    return int(lib().attn_bwd_workspace_bytes(B, H, Tq))
+
+
+def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None, workspace=None,
+             dq=None, dk=None, dv=None):
+    """Backward of attn_fwd: (dq, dk, dv) fp32 from the forward's inputs, its
+    output ``o`` and LSE, and the upstream gradient ``dout`` (bf16)."""
+    B, H, Tq, Tkv, d = _shape4(q, k, v)
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("o and dout must have q's shape")
+    if lse is None or tuple(lse.shape) != (B, H, Tq):
+        raise ValueError("lse [B, H, Tq] is required")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device) if dv is None else dv
+    wp, wbytes = _workspace(workspace, attn_bwd_workspace_bytes(B, H, Tq), q.device)
+    st = lib().attn_bwd(_dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16), _dev(v, "v", torch.bfloat16),
+                        _dev(o, "o", torch.bfloat16), _dev(dout, "dout", torch.bfloat16),
+                        _dev(lse, "lse", torch.float32), _dev(dq, "dq", torch.float32),
+                        _dev(dk, "dk", torch.float32), _dev(dv, "dv", torch.float32), B, H, Tq, Tkv, d,
+                        int(bool(causal)), scale, wp, wbytes, _stream())
+    _check(st)
+    return dq, dk, dv
+
+
+def prepared_bwd(q, k, v, o, lse, dout, dq, dk, dv, causal: bool, workspace, scale: float | None = None):
+    """Zero-argument callable enqueuing attn_bwd; see prepared_fwd."""
+    B, H, Tq, Tkv, d = _shape4(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    ptrs = [_dev(t, n, torch.bfloat16) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"))]
+    f32 = [_dev(t, n, torch.float32) for t, n in ((lse, "lse"), (dq, "dq"), (dk, "dk"), (dv, "dv"))]
+    wp, wb = _dev(workspace, "workspace", workspace.dtype), workspace.numel() * workspace.element_size()
+    fn = lib().attn_bwd
+    args = (*ptrs, *f32, B, H, Tq, Tkv, d, int(bool(causal)), scale, wp, wb, _stream())
+
+    def call():
+        _check(fn(*args))
+
+    return call
 
 
 def attn_last_kernel() -> str:

@@ -3,6 +3,7 @@
 // rejected call touches neither the device nor the runtime.
 #include "attn.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -241,6 +242,60 @@ int attn_decode_splits(int B, int Hq, int Hkv, int Tkv, int d) {
 int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Tkv, int d,
                 float scale, int num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     return attn_decode_gqa(q, k, v, o, lse, B, H, H, Tkv, d, scale, num_splits, workspace, workspace_bytes, stream);
+}
+
+size_t attn_bwd_workspace_bytes(int B, int H, int Tq) {
+    if (B < 1 || H < 1 || Tq < 1) return 0;
+    return attn::backward_workspace_bytes(B, H, Tq);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+             float* dq, float* dk, float* dv, int B, int H, int Tq, int Tkv, int d, int causal, float scale,
+             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    int st = check_common(q, k, v, o, nullptr, B, H, H, Tq, Tkv, d, causal, scale, 2);
+    if (st != ATTN_OK) return st;
+    if (!dout) return fail(ATTN_EINVAL, "dout is NULL");
+    if (!lse) return fail(ATTN_EINVAL, "lse is NULL (the backward pass recomputes P from it)");
+    if (!dq || !dk || !dv) return fail(ATTN_EINVAL, "dq, dk and dv must not be NULL");
+    if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+        return fail(ATTN_EINVAL, "dout, dq, dk and dv must be 16-byte aligned");
+    if (!aligned(lse, 4)) return fail(ATTN_EINVAL, "lse must be 4-byte aligned");
+    if (!attn::backward_supports(d)) return fail(ATTN_EUNSUPPORTED, "backward supports d = 64");
+    if (double(Tkv) * d * 2 >= 2147483648.0 || double(Tq) * d * 2 >= 2147483648.0)
+        return fail(ATTN_EUNSUPPORTED, "backward supports T*d*2 < 2^31 bytes per head");
+    if (double(B) * H * ((std::max(Tq, Tkv) + 127) / 128) > 2147483647.0) return fail(ATTN_EINVAL, "grid too large");
+    const size_t need = attn::backward_workspace_bytes(B, H, Tq);
+    if (!workspace) return fail(ATTN_EWORKSPACE, "workspace is NULL");
+    if (workspace_bytes < need)
+        return fail(ATTN_EWORKSPACE, "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " +
+                                         std::to_string(need));
+    // every input, output and the workspace must be disjoint
+    const uint64_t qb = uint64_t(B) * H * Tq * d * 2, kvb = uint64_t(B) * H * Tkv * d * 2;
+    const Range ins[6] = {{reinterpret_cast<uintptr_t>(q), reinterpret_cast<uintptr_t>(q) + qb, "q"},
+                          {reinterpret_cast<uintptr_t>(k), reinterpret_cast<uintptr_t>(k) + kvb, "k"},
+                          {reinterpret_cast<uintptr_t>(v), reinterpret_cast<uintptr_t>(v) + kvb, "v"},
+                          {reinterpret_cast<uintptr_t>(o), reinterpret_cast<uintptr_t>(o) + qb, "o"},
+                          {reinterpret_cast<uintptr_t>(dout), reinterpret_cast<uintptr_t>(dout) + qb, "dout"},
+                          {reinterpret_cast<uintptr_t>(lse), reinterpret_cast<uintptr_t>(lse) + uint64_t(B) * H * Tq * 4,
+                           "lse"}};
+    const Range outs[4] = {{reinterpret_cast<uintptr_t>(dq), reinterpret_cast<uintptr_t>(dq) + 2 * qb, "dq"},
+                           {reinterpret_cast<uintptr_t>(dk), reinterpret_cast<uintptr_t>(dk) + 2 * kvb, "dk"},
+                           {reinterpret_cast<uintptr_t>(dv), reinterpret_cast<uintptr_t>(dv) + 2 * kvb, "dv"},
+                           {reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need,
+                            "workspace"}};
+    for (int i = 0; i < 4; ++i) {
+        for (const Range& r : ins)
+            if (overlap(outs[i], r)) return fail(ATTN_EINVAL, std::string(outs[i].name) + " overlaps " + r.name);
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outs[j]))
+                return fail(ATTN_EINVAL, std::string(outs[i].name) + " overlaps " + outs[j].name);
+    }
+    if (!aligned(workspace, 16)) return fail(ATTN_EINVAL, "workspace must be 16-byte aligned");
+    attn::BackwardArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, H, Tq, Tkv, d, causal != 0,
+                         float(double(scale) * kLog2e), scale, workspace};
+    const char* name = nullptr;
+    (void)hipGetLastError();
+    return finish(attn::launch_backward_bf16(a, stream, &name), name);
 }
 
 const char* attn_last_kernel(void) { return g_last_kernel.c_str(); }

@@ -1,0 +1,543 @@
+// Exact attention backward, bf16 inputs, head width 64, gfx950.
+//
+// The softmax output is not stored by the forward pass; it is recomputed here
+// from Q, K, V and the saved per-row log-sum-exp ("IO-Aware Attention:
+// Tiling the Score Matrix Without Materializing It", section "What has to
+// stay in fast memory": the recomputation is one more pass over the score
+// blocks, paid in flops instead of bytes).  With c = scale * log2 e,
+// lse2 = lse * log2 e and D_i = sum_d dO_id O_id:
+//
+//   P  = exp2(c * Q K^T - lse2)         (recomputed per block, never stored)
+//   dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D)
+//   dQ = scale * dS K,   dK = scale * dS^T Q
+//
+// Three kernels, no atomics:
+// * bwd_stats: per query row (lse2, D) -- one streaming pass over O and dO.
+// * bwd_dkdv: one workgroup per 128-key tile (32 keys per wave, one key per
+//   lane column).  K and V of the wave stay in VGPRs as MFMA B operands; Q and
+//   dO blocks of 64 rows and their row statistics stream through a 3-stage
+//   LDS ring filled by DMA.  Per block: S = Q K^T and dP = dO V^T (Q, dO read
+//   as rows), then dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T read by
+//   ds_read_b64_tr_b16, so P and dS go from the accumulator layout to the B
+//   operand with only a bf16 pack.
+// * bwd_dq: one workgroup per 128-query tile, the forward's layout (one query
+//   per lane): S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T with K^T read
+//   transposed from the ring.
+// Q and dO (in bwd_dkdv) and K (in bwd_dq) are read both as rows and
+// transposed, so their LDS chunk swizzle is conflict-free for both patterns.
+// Products are bf16 MFMA with fp32 accumulation; P and dS are rounded to
+// bf16 (nearest even) as MFMA operands; dQ, dK, dV are written in fp32.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace attn {
+namespace {
+
+constexpr int D = 64;
+constexpr int ROWB = D * 2;       // bytes per row
+constexpr int TQ = D / 16;        // k-steps over d
+constexpr int DT = D / 32;        // 32-column tiles over d
+
+// One swizzle for 128-byte rows read both ways: 16 consecutive rows map
+// their chunk c to 8 distinct chunks x 2 bank halves (row reads of 32 rows x
+// one chunk pair), and rows r, r+1 vs r+2, r+3 land in different 64-byte
+// halves (transposed reads of 8 rows x 64 bytes).
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) & 7) ^ (((row >> 1) & 1) << 2); }
+
+// Byte offset of the 8-byte piece holding columns col..col+3 of a swizzled row.
+__device__ __forceinline__ uint32_t tr_off(int row, int col) {
+    return (uint32_t)(row * ROWB + ((((col >> 3) ^ swz(row)) << 4) | ((col & 4) << 1)));
+}
+
+// Four transposed reads for the 16-row k-step STP of a 32-row group at byte
+// `base`: the two 32-column tiles, rows 16 STP + (0..7) and + 8.  Rows r and
+// r + 8 differ in their swizzle, rows r and r + 16 do not, so each tile keeps
+// one offset per 8-row half and the k-step is an immediate.
+template <int STP>
+__device__ __forceinline__ void tr_kstep(uint32_t base, const uint32_t (&o)[DT][2], u32x4_t& a0, u32x4_t& a1) {
+    u32x2_t l0 = lds_read_tr16_b64<STP * 16 * ROWB>(base + o[0][0]);
+    u32x2_t h0 = lds_read_tr16_b64<STP * 16 * ROWB>(base + o[0][1]);
+    u32x2_t l1 = lds_read_tr16_b64<STP * 16 * ROWB>(base + o[1][0]);
+    u32x2_t h1 = lds_read_tr16_b64<STP * 16 * ROWB>(base + o[1][1]);
+    lgkm_wait_4(l0, h0, l1, h1);
+    a0 = u32x4_t{l0[0], l0[1], h0[0], h0[1]};
+    a1 = u32x4_t{l1[0], l1[1], h1[0], h1[1]};
+}
+
+// ---------------------------------------------------------------- statistics
+
+// stats[bh * Tq + i] = (lse_i * log2 e, sum_d dO_id O_id); 8 lanes per row.
+__global__ __launch_bounds__(256)
+void bwd_stats_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
+                      const float* __restrict__ LSE, float2* __restrict__ stats, long long rows) {
+    const long long r = (long long)blockIdx.x * 32 + (threadIdx.x >> 3);
+    const int part = threadIdx.x & 7;
+    float acc = 0.f;
+    if (r < rows) {
+        const u32x4_t o = *reinterpret_cast<const u32x4_t*>(O + r * D + 8 * part);
+        const u32x4_t g = *reinterpret_cast<const u32x4_t*>(dO + r * D + 8 * part);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc = __builtin_fmaf(bf16_lo(o[i]), bf16_lo(g[i]), acc);
+            acc = __builtin_fmaf(bf16_hi(o[i]), bf16_hi(g[i]), acc);
+        }
+    }
+    acc = group_sum<8>(acc);
+    if (r < rows && part == 0) stats[r] = make_float2(LSE[r] * 1.44269504088896340736f, acc);
+}
+
+// ------------------------------------------------------------------ dK, dV
+
+constexpr int KV_WAVES = 4;
+constexpr int BKV = 32 * KV_WAVES;   // keys per workgroup
+constexpr int BQ2 = 64;              // query rows per streamed block
+constexpr int NS = 3;                // ring stages
+constexpr int QBLK = BQ2 * ROWB;     // 8 KiB
+constexpr int STAGE = 2 * QBLK + 1024;
+constexpr int KV_LI = QBLK / 1024 / KV_WAVES;   // DMA instructions per wave per operand per block
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(KV_WAVES * 64, 2)
+void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                     const float2* __restrict__ stats, float* __restrict__ dK, float* __restrict__ dV,
+                     int Tq, int Tkv, int BH, int nkt, float c, float scale) {
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[NS][STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int ln = lane & 31;
+    const int hf = lane >> 5;
+
+    // causal: the first key tiles see the most query rows, so they go first
+    const int bh = blockIdx.x % BH;
+    const int kt = blockIdx.x / BH;
+    const int k0 = kt * BKV;
+    const int off = Tkv - Tq;
+    const int key = k0 + 32 * wave + ln;        // this lane's key column
+
+    const size_t qbase = (size_t)bh * Tq * D;
+    const size_t kvbase = (size_t)bh * Tkv * D;
+
+    // K and V fragments (B operands): key `key`, d = 16t + 8hf + (0..7)
+    bf16x8_t kf[TQ], vf[TQ];
+    if (key < Tkv) {
+        const u32x4_t* ks = reinterpret_cast<const u32x4_t*>(K + kvbase + (size_t)key * D + 8 * hf);
+        const u32x4_t* vs = reinterpret_cast<const u32x4_t*>(V + kvbase + (size_t)key * D + 8 * hf);
+#pragma unroll
+        for (int t = 0; t < TQ; ++t) {
+            kf[t] = __builtin_bit_cast(bf16x8_t, ks[2 * t]);
+            vf[t] = __builtin_bit_cast(bf16x8_t, vs[2 * t]);
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < TQ; ++t) {
+            kf[t] = __builtin_bit_cast(bf16x8_t, u32x4_t{0, 0, 0, 0});
+            vf[t] = kf[t];
+        }
+    }
+
+    // query blocks that see any key of this tile (bottom-right causal)
+    const int nqb = (Tq + BQ2 - 1) / BQ2;
+    const int qb_first = CAUSAL ? max(0, k0 - off) / BQ2 : 0;
+    // blocks from qb_free on are visible to every key of the tile and full
+    const int tile_last_key = min(k0 + BKV, Tkv) - 1;
+    int qb_free = CAUSAL ? (max(0, tile_last_key - off) + BQ2 - 1) / BQ2 : 0;
+    qb_free = max(qb_free, qb_first);
+    const int qb_full_end = Tq / BQ2;             // blocks before this have no ragged rows
+
+    // DMA: wave w moves row groups g = w + 4i (8 rows = 1 KiB) of Q and dO,
+    // and every wave moves the block's 512 bytes of row statistics
+    uint32_t voff[KV_LI];
+#pragma unroll
+    for (int i = 0; i < KV_LI; ++i) {
+        const int g = wave + KV_WAVES * i;
+        const int row = 8 * g + (lane >> 3);
+        voff[i] = (uint32_t)(row * ROWB + (((lane & 7) ^ swz(row)) << 4));
+    }
+    auto issue = [&](int j) {
+        const bool live = j < nqb;
+        const int q0 = j * BQ2;
+        const uint32_t bytes = live ? (uint32_t)(Tq - q0) * (uint32_t)ROWB : 0u;
+        const size_t eoff = live ? (size_t)q0 * D : 0;
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + qbase + eoff, bytes);
+        const __amdgpu_buffer_rsrc_t rg = make_rsrc(dO + qbase + eoff, bytes);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(stats + (size_t)bh * Tq + (live ? q0 : 0),
+                                                    live ? (uint32_t)(Tq - q0) * 8u : 0u);
+        uint8_t* st = &ring[j % NS][0];
+#pragma unroll
+        for (int i = 0; i < KV_LI; ++i) {
+            const int g = wave + KV_WAVES * i;
+            buffer_load_lds_b128(rq, voff[i], st + g * 1024);
+            buffer_load_lds_b128(rg, voff[i], st + QBLK + g * 1024);
+        }
+        buffer_load_lds_b128(rs, (uint32_t)lane * 16u, st + 2 * QBLK);
+    };
+
+    // row-read offsets (A operand of S = Q K^T and dP = dO V^T): row ln, chunk 2t + hf
+    uint32_t r_off[TQ];
+#pragma unroll
+    for (int t = 0; t < TQ; ++t) r_off[t] = (uint32_t)(ln * ROWB + (((2 * t + hf) ^ swz(ln)) << 4));
+    // transposed-read offsets (A operand of dV^T = dO^T P, dK^T = Q^T dS): lane group
+    // lg = lane / 16, jj = lane % 16 addresses row 4(lg/2) + jj/4 (+8), columns
+    // 32dt + 16(lg%2) + 4(jj%4)
+    uint32_t t_off[DT][2];
+    {
+        const int lg = lane >> 4, jj = lane & 15;
+        const int row = 4 * (lg >> 1) + (jj >> 2);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const int col = 32 * dt + 16 * (lg & 1) + 4 * (jj & 3);
+            t_off[dt][0] = tr_off(row, col);
+            t_off[dt][1] = tr_off(row + 8, col);
+        }
+    }
+
+    f32x16_t dkt[DT], dvt[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            dkt[dt][r] = 0.f;
+            dvt[dt][r] = 0.f;
+        }
+
+    // one 32-row sub-tile qs of the block staged at `st`; q0 = first row of the block
+    auto subtile = [&](const uint8_t* st, int q0, int qs, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        const uint8_t* qst = st;
+        const uint8_t* gst = st + QBLK;
+        const float* sst = reinterpret_cast<const float*>(st + 2 * QBLK);
+        f32x16_t s, dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            s[r] = 0.f;
+            dp[r] = 0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < TQ; ++t) {
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(qst + r_off[t] + qs * 32 * ROWB);
+            const bf16x8_t g = *reinterpret_cast<const bf16x8_t*>(gst + r_off[t] + qs * 32 * ROWB);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[t], s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(g, vf[t], dp, 0, 0, 0);
+        }
+        // element r of this lane: query row qs*32 + 8(r/4) + 4hf + r%4 of the block, key `key`
+        uint32_t pw[8], dw[8];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const int rb = qs * 32 + 8 * g4 + 4 * hf;           // first of 4 consecutive rows
+            const f32x4_t st0 = *reinterpret_cast<const f32x4_t*>(sst + 2 * rb);      // (lse2, D) rows rb, rb+1
+            const f32x4_t st1 = *reinterpret_cast<const f32x4_t*>(sst + 2 * rb + 4);  // rows rb+2, rb+3
+            float p[4], ds[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float lse2 = (i < 2) ? st0[2 * i] : st1[2 * (i - 2)];
+                const float dd = (i < 2) ? st0[2 * i + 1] : st1[2 * (i - 2) + 1];
+                const int r = 4 * g4 + i;
+                float pe = fast_exp2(__builtin_fmaf(s[r], c, -lse2));
+                if constexpr (MASK) {
+                    const int qrow = q0 + rb + i;
+                    if (qrow >= Tq || (CAUSAL && key > qrow + off)) pe = 0.f;
+                }
+                p[i] = pe;
+                ds[i] = pe * (dp[r] - dd);
+            }
+            pw[2 * g4] = pack_bf16x2(p[0], p[1]);
+            pw[2 * g4 + 1] = pack_bf16x2(p[2], p[3]);
+            dw[2 * g4] = pack_bf16x2(ds[0], ds[1]);
+            dw[2 * g4 + 1] = pack_bf16x2(ds[2], ds[3]);
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS over the sub-tile's 32 rows (two 16-row k-steps)
+        const uint32_t gb = lds_addr(gst) + qs * 32 * ROWB;
+        const uint32_t qb = lds_addr(qst) + qs * 32 * ROWB;
+        auto kstep = [&](auto stp_tag) {
+            constexpr int stp = decltype(stp_tag)::value;
+            const u32x4_t pv = {pw[4 * stp], pw[4 * stp + 1], pw[4 * stp + 2], pw[4 * stp + 3]};
+            const u32x4_t dv = {dw[4 * stp], dw[4 * stp + 1], dw[4 * stp + 2], dw[4 * stp + 3]};
+            const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pv);
+            const bf16x8_t db = __builtin_bit_cast(bf16x8_t, dv);
+            u32x4_t a0, a1;
+            tr_kstep<stp>(gb, t_off, a0, a1);
+            dvt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a0), pb, dvt[0], 0, 0, 0);
+            dvt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a1), pb, dvt[1], 0, 0, 0);
+            tr_kstep<stp>(qb, t_off, a0, a1);
+            dkt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a0), db, dkt[0], 0, 0, 0);
+            dkt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a1), db, dkt[1], 0, 0, 0);
+        };
+        kstep(std::integral_constant<int, 0>{});
+        kstep(std::integral_constant<int, 1>{});
+    };
+
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j) issue(qb_first + j);
+    for (int j = qb_first; j < nqb; ++j) {
+        wait_vmcnt<(2 * KV_LI + 1) * (NS - 2)>();   // this wave's part of block j has landed
+        __syncthreads();                            // ... everyone's, and stage (j-1) % NS is free
+        issue(j + NS - 1);
+        const uint8_t* st = &ring[j % NS][0];
+        const int q0 = j * BQ2;
+        const bool free_blk = (j >= qb_free) && (j < qb_full_end);
+        // one sub-tile at a time (not unrolled: the two would double the live registers)
+#pragma nounroll
+        for (int qs = 0; qs < 2; ++qs) {
+            if (free_blk) {
+                subtile(st, q0, qs, std::false_type{});
+            } else if (!CAUSAL || q0 + 32 * qs + 31 + off >= k0 + 32 * wave) {
+                // a wave whose keys all lie right of every row of a sub-tile skips it
+                subtile(st, q0, qs, std::true_type{});
+            }
+        }
+    }
+    wait_vmcnt<0>();    // no DMA may still be writing LDS when the workgroup retires
+
+    // dK = scale * (dK^T)^T, dV = (dV^T)^T: lane = key column, element r = d 32dt + 8(r/4) + 4hf + r%4
+    if (key < Tkv) {
+        float* dkrow = dK + kvbase + (size_t)key * D;
+        float* dvrow = dV + kvbase + (size_t)key * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                float4 a, b;
+                a.x = dkt[dt][4 * g4] * scale;
+                a.y = dkt[dt][4 * g4 + 1] * scale;
+                a.z = dkt[dt][4 * g4 + 2] * scale;
+                a.w = dkt[dt][4 * g4 + 3] * scale;
+                b.x = dvt[dt][4 * g4];
+                b.y = dvt[dt][4 * g4 + 1];
+                b.z = dvt[dt][4 * g4 + 2];
+                b.w = dvt[dt][4 * g4 + 3];
+                *reinterpret_cast<float4*>(dkrow + 32 * dt + 8 * g4 + 4 * hf) = a;
+                *reinterpret_cast<float4*>(dvrow + 32 * dt + 8 * g4 + 4 * hf) = b;
+            }
+    }
+}
+
+// ----------------------------------------------------------------------- dQ
+
+constexpr int DQ_WAVES = 4;
+constexpr int BQ = 32 * DQ_WAVES;   // query rows per workgroup
+constexpr int BK = 64;              // keys per streamed block
+constexpr int KBLK = BK * ROWB;     // 8 KiB
+constexpr int DQ_LI = KBLK / 1024 / DQ_WAVES;
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(DQ_WAVES * 64, 2)
+void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                   const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                   const float2* __restrict__ stats, float* __restrict__ dQ,
+                   int Tq, int Tkv, int BH, int nqt, float c, float scale) {
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[NS][2][KBLK];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int ln = lane & 31;
+    const int hf = lane >> 5;
+
+    const int bh = blockIdx.x % BH;
+    const int rank = blockIdx.x / BH;
+    const int qt = CAUSAL ? (nqt - 1 - rank) : rank;   // heaviest tiles first
+    const int q0 = qt * BQ;
+    const int off = Tkv - Tq;
+    const size_t qbase = (size_t)bh * Tq * D;
+    const size_t kvbase = (size_t)bh * Tkv * D;
+    const uint16_t* Kh = K + kvbase;
+    const uint16_t* Vh = V + kvbase;
+
+    // Q and dO fragments (B operands): row q0 + 32*wave + ln, d = 16t + 8hf + (0..7)
+    const int qrow = q0 + wave * 32 + ln;
+    bf16x8_t qf[TQ], gf[TQ];
+    float lse2 = 0.f, dd = 0.f;
+    if (qrow < Tq) {
+        const u32x4_t* qs = reinterpret_cast<const u32x4_t*>(Q + qbase + (size_t)qrow * D + 8 * hf);
+        const u32x4_t* gs = reinterpret_cast<const u32x4_t*>(dO + qbase + (size_t)qrow * D + 8 * hf);
+#pragma unroll
+        for (int t = 0; t < TQ; ++t) {
+            qf[t] = __builtin_bit_cast(bf16x8_t, qs[2 * t]);
+            gf[t] = __builtin_bit_cast(bf16x8_t, gs[2 * t]);
+        }
+        const float2 sv = stats[(size_t)bh * Tq + qrow];
+        lse2 = sv.x;
+        dd = sv.y;
+    } else {
+#pragma unroll
+        for (int t = 0; t < TQ; ++t) {
+            qf[t] = __builtin_bit_cast(bf16x8_t, u32x4_t{0, 0, 0, 0});
+            gf[t] = qf[t];
+        }
+    }
+
+    const int kend = CAUSAL ? min(Tkv, q0 + BQ + off) : Tkv;
+    const int nblk = (kend + BK - 1) / BK;
+    const int wq_last = q0 + wave * 32 + 31;
+    const int lim = CAUSAL ? min(Tkv - 1, qrow + off) : (Tkv - 1);   // last key this row sees
+
+    uint32_t voff[DQ_LI];
+#pragma unroll
+    for (int i = 0; i < DQ_LI; ++i) {
+        const int g = wave + DQ_WAVES * i;
+        const int row = 8 * g + (lane >> 3);
+        voff[i] = (uint32_t)(row * ROWB + (((lane & 7) ^ swz(row)) << 4));
+    }
+    auto issue = [&](int j) {
+        const int kb = j * BK;
+        const bool live = j < nblk;
+        const uint32_t bytes = live ? (uint32_t)(Tkv - kb) * (uint32_t)ROWB : 0u;
+        const size_t eoff = live ? (size_t)kb * D : 0;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + eoff, bytes);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + eoff, bytes);
+        uint8_t* st = &ring[j % NS][0][0];
+#pragma unroll
+        for (int i = 0; i < DQ_LI; ++i) {
+            const int g = wave + DQ_WAVES * i;
+            buffer_load_lds_b128(rk, voff[i], st + g * 1024);
+            buffer_load_lds_b128(rv, voff[i], st + KBLK + g * 1024);
+        }
+    };
+
+    uint32_t r_off[TQ];
+#pragma unroll
+    for (int t = 0; t < TQ; ++t) r_off[t] = (uint32_t)(ln * ROWB + (((2 * t + hf) ^ swz(ln)) << 4));
+    uint32_t t_off[DT][2];
+    {
+        const int lg = lane >> 4, jj = lane & 15;
+        const int row = 4 * (lg >> 1) + (jj >> 2);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const int col = 32 * dt + 16 * (lg & 1) + 4 * (jj & 3);
+            t_off[dt][0] = tr_off(row, col);
+            t_off[dt][1] = tr_off(row + 8, col);
+        }
+    }
+
+    f32x16_t dqt[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dqt[dt][r] = 0.f;
+
+    auto step = [&](const uint8_t* kst, int kb, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        const uint8_t* vst = kst + KBLK;
+        // S^T and dP^T for the block's 64 keys (two 32-key tiles); lane = query column
+        uint32_t dw[16];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            f32x16_t s, dp;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                s[r] = 0.f;
+                dp[r] = 0.f;
+            }
+#pragma unroll
+            for (int t = 0; t < TQ; ++t) {
+                const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kst + r_off[t] + kt * 32 * ROWB);
+                const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(vst + r_off[t] + kt * 32 * ROWB);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, gf[t], dp, 0, 0, 0);
+            }
+            float ds[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float pe = fast_exp2(__builtin_fmaf(s[r], c, -lse2));
+                if constexpr (MASK) {
+                    const int kk = kb + 32 * kt + 8 * (r >> 2) + 4 * hf + (r & 3);
+                    if (kk > lim) pe = 0.f;
+                }
+                ds[r] = pe * (dp[r] - dd);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) dw[8 * kt + i] = pack_bf16x2(ds[2 * i], ds[2 * i + 1]);
+        }
+        // dQ^T += K^T dS^T: four 16-key k-steps
+        const uint32_t kbase = lds_addr(kst);
+        auto kstep = [&](auto stp_tag) {
+            constexpr int stp = decltype(stp_tag)::value;
+            const u32x4_t dv = {dw[4 * stp], dw[4 * stp + 1], dw[4 * stp + 2], dw[4 * stp + 3]};
+            const bf16x8_t db = __builtin_bit_cast(bf16x8_t, dv);
+            u32x4_t a0, a1;
+            tr_kstep<stp>(kbase, t_off, a0, a1);
+            dqt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a0), db, dqt[0], 0, 0, 0);
+            dqt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a1), db, dqt[1], 0, 0, 0);
+        };
+        kstep(std::integral_constant<int, 0>{});
+        kstep(std::integral_constant<int, 1>{});
+        kstep(std::integral_constant<int, 2>{});
+        kstep(std::integral_constant<int, 3>{});
+    };
+
+    const int nfull = CAUSAL ? min(Tkv / BK, (q0 + off + 1) / BK) : Tkv / BK;
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j) issue(j);
+    int j = 0;
+    for (; j < nfull; ++j) {
+        wait_vmcnt<2 * DQ_LI * (NS - 2)>();
+        __syncthreads();
+        issue(j + NS - 1);
+        step(&ring[j % NS][0][0], j * BK, std::false_type{});
+    }
+    for (; j < nblk; ++j) {
+        wait_vmcnt<2 * DQ_LI * (NS - 2)>();
+        __syncthreads();
+        issue(j + NS - 1);
+        const int kb = j * BK;
+        if (!CAUSAL || kb <= wq_last + off) step(&ring[j % NS][0][0], kb, std::true_type{});
+    }
+    wait_vmcnt<0>();
+
+    // dQ = scale * (dQ^T)^T: lane = query row, element r = d 32dt + 8(r/4) + 4hf + r%4
+    if (qrow < Tq) {
+        float* row = dQ + qbase + (size_t)qrow * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                float4 a;
+                a.x = dqt[dt][4 * g4] * scale;
+                a.y = dqt[dt][4 * g4 + 1] * scale;
+                a.z = dqt[dt][4 * g4 + 2] * scale;
+                a.w = dqt[dt][4 * g4 + 3] * scale;
+                *reinterpret_cast<float4*>(row + 32 * dt + 8 * g4 + 4 * hf) = a;
+            }
+    }
+}
+
+template <bool CAUSAL>
+hipError_t launch_bwd_c(const BackwardArgs& a, hipStream_t stream) {
+    const int BHn = a.B * a.H;
+    const long long rows = (long long)BHn * a.Tq;
+    float2* stats = static_cast<float2*>(a.workspace);
+    hipLaunchKernelGGL(bwd_stats_kernel, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout), a.lse, stats, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nkt = (a.Tkv + BKV - 1) / BKV;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<CAUSAL>), dim3((unsigned)(nkt * BHn)), dim3(KV_WAVES * 64), 0, stream,
+                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                       static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), stats, a.dk, a.dv,
+                       a.Tq, a.Tkv, BHn, nkt, a.c, a.scale);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int nqt = (a.Tq + BQ - 1) / BQ;
+    hipLaunchKernelGGL((bwd_dq_kernel<CAUSAL>), dim3((unsigned)(nqt * BHn)), dim3(DQ_WAVES * 64), 0, stream,
+                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                       static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), stats, a.dq,
+                       a.Tq, a.Tkv, BHn, nqt, a.c, a.scale);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool backward_supports(int d) { return d == D; }
+
+size_t backward_workspace_bytes(int B, int H, int Tq) { return (size_t)B * H * Tq * sizeof(float2); }
+
+hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream, const char** name) {
+    *name = a.causal ? "bwd_bf16_d64<stats+dkdv(bk=128,bq=64)+dq(bq=128,bk=64),causal>"
+                     : "bwd_bf16_d64<stats+dkdv(bk=128,bq=64)+dq(bq=128,bk=64)>";
+    if (a.causal) return launch_bwd_c<true>(a, stream);
+    return launch_bwd_c<false>(a, stream);
+}
+
+}  // namespace attn

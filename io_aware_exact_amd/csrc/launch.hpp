@@ -46,6 +46,27 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, const PrefillSplit& split, 
                                const char** name);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream, const char** name);
 bool prefill_f32_supports(int d);
+struct BackwardArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const void* dout;
+    const float* lse;
+    float* dq;
+    float* dk;
+    float* dv;
+    int B, H, Tq, Tkv, d;
+    bool causal;
+    float c;          // scale * log2(e)
+    float scale;
+    void* workspace;  // per query row (lse * log2 e, D) as float2
+};
+
+bool backward_supports(int d);
+size_t backward_workspace_bytes(int B, int H, int Tq);
+hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream, const char** name);
+
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream, const char** name);
 int decode_auto_splits(int B, int Hq, int Hkv, int Tkv, int d);
 

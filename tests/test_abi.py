@@ -73,6 +73,17 @@ def fsplit(lib, **kw):
                               a["causal"], a["scale"], a["chunk"], a["ws"], a["wsb"], a["stream"])
 
 
+DO, DQ, DK, DV = (0x10_0000_0000 * i for i in range(7, 11))
+
+
+def bwd(lib, **kw):
+    a = dict(q=Q, k=K, v=V, o=O, do=DO, lse=L, dq=DQ, dk=DK, dv=DV, B=2, H=3, Tq=64, Tkv=80, d=64, causal=1,
+             scale=0.125, ws=W, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.attn_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["B"],
+                        a["H"], a["Tq"], a["Tkv"], a["d"], a["causal"], a["scale"], a["ws"], a["wsb"], a["stream"])
+
+
 def gqa(lib, **kw):
     a = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, Hq=8, Hkv=2, Tkv=100, d=128, scale=0.088, P=4, ws=W, wsb=1 << 30,
              stream=None)
@@ -190,6 +201,24 @@ def test_decode_automatic_splits():
     assert attn.attn_decode_splits(1, 12, 5, 1024, 64) == 0
     assert attn.attn_decode_splits(1, 12, 12, 1024, 96) == 0
     assert attn.attn_decode_splits(0, 12, 12, 1024, 64) == 0
+
+
+def test_backward_arguments(lib):
+    for bad, want in [(dict(do=None), "dout is NULL"), (dict(lse=None), "lse is NULL"), (dict(dq=None), "NULL"),
+                      (dict(dk=None), "NULL"), (dict(dv=None), "NULL"), (dict(q=None), "q is NULL"),
+                      (dict(dq=DQ + 4), "aligned"), (dict(do=DO + 2), "aligned"), (dict(lse=L + 1), "aligned"),
+                      (dict(causal=1, Tq=81), "Tq <= Tkv"), (dict(scale=0.0), "scale"),
+                      (dict(dq=Q + 64), "dq overlaps q"), (dict(dk=DQ + 256), "dq overlaps dk"),
+                      (dict(ws=DV + 16), "dv overlaps workspace"), (dict(ws=W + 8), "aligned")]:
+        st = bwd(lib, **bad)
+        assert st == EINVAL, bad
+        assert want in attn.attn_status_string(st), (bad, attn.attn_status_string(st))
+    assert bwd(lib, d=128) == EUNSUP and "d = 64" in attn.attn_status_string(EUNSUP)
+    assert bwd(lib, ws=None) == EWS
+    need = attn.attn_bwd_workspace_bytes(2, 3, 64)
+    assert need == 2 * 3 * 64 * 8
+    assert bwd(lib, wsb=need - 1) == EWS and str(need) in attn.attn_status_string(EWS)
+    assert attn.attn_bwd_workspace_bytes(0, 3, 64) == 0
 
 
 def test_workspace_size_formula():
