@@ -197,6 +197,11 @@ def test_decode_automatic_splits():
     # grouped-query: workgroups count kv heads x head tiles (groups of 4 -> one tile)
     assert attn.attn_decode_splits(64, 32, 8, 8192, 128) == 1
     assert attn.attn_decode_splits(4, 32, 8, 8192, 128) == 16
+    # groups of 8 or more: the MFMA kernel, one wave per (batch, kv head, 32-head tile), up to 64
+    assert attn.attn_decode_splits(64, 32, 4, 8192, 128) == 2
+    assert attn.attn_decode_splits(64, 32, 1, 8192, 128) == 8
+    assert attn.attn_decode_splits(1, 32, 4, 16384, 128) == 64
+    assert attn.attn_decode_splits(1, 64, 1, 16384, 128) == 64   # 2 head tiles
     # invalid / unsupported
     assert attn.attn_decode_splits(1, 12, 5, 1024, 64) == 0
     assert attn.attn_decode_splits(1, 12, 12, 1024, 96) == 0
