@@ -129,7 +129,7 @@ size_t attn_decode_workspace_bytes(int B, int H, int d, int num_splits);
 /*
  * attn_decode_splits -- the number of key partitions the library picks for a
  * decode step (num_splits = 0): enough for about 512 workgroups (at most 32
- * partitions; 64 for groups of 8 or more query heads, whose kernel runs one
+ * partitions; 64 for groups of 4 or more query heads, whose kernel runs one
  * wave per workgroup), and none holding less than 64 KiB of K and V
  * (16384/d keys).  A single sequence offers only H
  * independent heads, too few to occupy the chip; splitting the key axis is
@@ -174,7 +174,10 @@ int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse
  *   workspace  at least attn_decode_workspace_bytes(B,Hq,d,num_splits) bytes
  *   other arguments as attn_decode.
  *
- * Errors: ATTN_EINVAL also when Hkv < 1 or Hq % Hkv != 0.  Supported: d in {64, 128}.
+ * Groups of 4 or more query heads run on the matrix cores (the heads of a
+ * group are the columns of an MFMA tile); smaller groups on the vector ALUs.
+ * Errors: ATTN_EINVAL also when Hkv < 1 or Hq % Hkv != 0.  Supported: d in
+ * {64, 128}, Tkv*d*2 < 2^31 bytes per head (also for attn_decode).
  */
 int attn_decode_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
                     int B, int Hq, int Hkv, int Tkv, int d, float scale, int num_splits,

@@ -218,6 +218,9 @@ int attn_decode_gqa(const void* q, const void* k, const void* v, void* o, float*
     if (st != ATTN_OK) return st;
     if (num_splits < 0) return fail(ATTN_EINVAL, "num_splits must be >= 0");
     if (d != 64 && d != 128) return fail(ATTN_EUNSUPPORTED, "decode supports d in {64, 128}");
+    // buffer-load ranges are 32-bit byte counts per (batch, kv head)
+    if (double(Tkv) * d * 2 >= 2147483648.0)
+        return fail(ATTN_EUNSUPPORTED, "decode supports Tkv*d*2 < 2^31 bytes per head");
     if (num_splits == 0) num_splits = attn::decode_auto_splits(B, Hq, Hkv, Tkv, d);
     const int splits = num_splits > Tkv ? Tkv : num_splits;
     if (splits > 65535) return fail(ATTN_EUNSUPPORTED, "decode supports at most 65535 partitions");

@@ -71,6 +71,12 @@ __device__ __forceinline__ void buffer_load_lds_b128(__amdgpu_buffer_rsrc_t r, u
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 16, (int)voff, 0, 0, 0);
 }
 
+// The same with the non-temporal cache policy, for data streamed exactly once
+// (a decode step's K/V cache): the lines are not kept in L2/MALL.
+__device__ __forceinline__ void buffer_load_lds_b128_stream(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 16, (int)voff, 0, 0, 2 /* nt */);
+}
+
 // Workgroup barrier without a memory fence.  __syncthreads() also waits for
 // every outstanding vector-memory operation, which would drain the LDS DMA
 // prefetch ring; callers that only need LDS data published wait for the DMA

@@ -40,8 +40,8 @@ namespace {
 
 constexpr int NW = 4;   // waves per workgroup
 // groups of at least this many query heads per key/value head use the MFMA
-// kernel (measured: at 4 heads the two kernels tie, from 8 on MFMA wins)
-constexpr int kMfmaMinGroup = 8;
+// kernel (measured: below 4 the two kernels tie, from 4 on MFMA wins)
+constexpr int kMfmaMinGroup = 4;
 
 template <int D, int GT>
 struct DecodeShape {
@@ -261,7 +261,7 @@ void decode_combine_kernel(const float* __restrict__ part, uint16_t* __restrict_
 // (lanes l and l + 32 hold the two key halves of head l % 32) and the softmax
 // state is per lane.  One wave per workgroup per (batch, kv head, head tile,
 // partition): the wave streams its partition's K/V blocks through a private
-// NS-stage LDS ring by DMA (no barriers), K read as rows, V with
+// NS-stage LDS ring by non-temporal DMA (no barriers), K read as rows, V with
 // ds_read_b64_tr_b16.  The reference max is raised lazily as in prefill (when
 // a head's block sum would exceed 2^16 or is not finite).  Partial records
 // and the combine kernel are those of the VALU kernel.
@@ -342,8 +342,9 @@ void decode_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
         for (int i = 0; i < LI; ++i) {
             const int row = RPG * i + lane / CPR;
             const int slot = lane % CPR;
-            buffer_load_lds_b128(rk, (uint32_t)(row * ROWB + ((slot ^ Gm::swz_k(row)) << 4)), st + i * 1024);
-            buffer_load_lds_b128(rv, (uint32_t)(row * ROWB + ((slot ^ Gm::swz_v(row)) << 4)), st + TILEB + i * 1024);
+            buffer_load_lds_b128_stream(rk, (uint32_t)(row * ROWB + ((slot ^ Gm::swz_k(row)) << 4)), st + i * 1024);
+            buffer_load_lds_b128_stream(rv, (uint32_t)(row * ROWB + ((slot ^ Gm::swz_v(row)) << 4)),
+                                        st + TILEB + i * 1024);
         }
     };
 
@@ -521,7 +522,7 @@ hipError_t launch_dg(const DecodeArgs& a, hipStream_t stream, const char** name)
     return e;
 }
 
-constexpr int kMfmaStages = 2;
+constexpr int kMfmaStages = 3;
 
 template <int D>
 hipError_t launch_mfma(const DecodeArgs& a, hipStream_t stream, const char** name) {

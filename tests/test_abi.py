@@ -138,6 +138,7 @@ def test_gqa_decode_arguments(lib):
     assert gqa(lib, Hkv=16) == EINVAL
     assert gqa(lib, Hq=0) == EINVAL
     assert gqa(lib, d=96) == EUNSUP
+    assert gqa(lib, Tkv=1 << 23, d=128) == EUNSUP and "2^31" in attn.attn_status_string(EUNSUP)
     assert gqa(lib, P=-1) == EINVAL
     assert gqa(lib, ws=None) == EWS
     # the workspace is sized by query heads
@@ -194,10 +195,12 @@ def test_decode_automatic_splits():
     assert attn.attn_decode_splits(1, 32, 32, 1024, 128) == 8
     assert attn.attn_decode_splits(16, 12, 12, 16384, 64) == 4    # 192 workgroups -> x4
     assert attn.attn_decode_splits(64, 32, 32, 8192, 128) == 1    # 2048 workgroups already
-    # grouped-query: workgroups count kv heads x head tiles (groups of 4 -> one tile)
+    # grouped-query: workgroups count kv heads x head tiles
+    assert attn.attn_decode_splits(64, 32, 16, 8192, 128) == 1     # groups of 2: VALU kernel, 4-wave groups
+    assert attn.attn_decode_splits(4, 32, 16, 8192, 128) == 8
     assert attn.attn_decode_splits(64, 32, 8, 8192, 128) == 1
     assert attn.attn_decode_splits(4, 32, 8, 8192, 128) == 16
-    # groups of 8 or more: the MFMA kernel, one wave per (batch, kv head, 32-head tile), up to 64
+    # groups of 4 or more: the MFMA kernel, one wave per (batch, kv head, 32-head tile), up to 64
     assert attn.attn_decode_splits(64, 32, 4, 8192, 128) == 2
     assert attn.attn_decode_splits(64, 32, 1, 8192, 128) == 8
     assert attn.attn_decode_splits(1, 32, 4, 16384, 128) == 64

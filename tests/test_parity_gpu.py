@@ -272,6 +272,7 @@ def gqa_check(w: Workload):
     (1, 4, 1, 1, 128, 16),       # a single cached key
     (2, 8, 2, 3000, 128, 0),     # automatic partitions
     (1, 64, 1, 700, 128, 5),     # groups of 64: two 32-head tiles per kv head (matrix-core kernel)
+    (2, 8, 2, 777, 64, 0),       # groups of 4 at d = 64, automatic partitions
     (2, 40, 1, 333, 64, 3),      # groups of 40: a partial second tile
     (3, 16, 2, 1, 64, 4),        # groups of 8 against a single key
     (1, 32, 4, 5000, 128, 0),    # groups of 8, automatic partitions
@@ -281,7 +282,7 @@ def test_gqa_decode_shapes(B, Hq, Hkv, Tkv, d, splits):
                               seed=40 + Hq + Tkv, num_splits=splits, Hkv=Hkv))
     used = splits if splits else attn.attn_decode_splits(B, Hq, Hkv, Tkv, d)
     assert ("combine" in kern) == (min(used, Tkv) > 1)
-    assert kern.startswith("decode_mfma") == (Hq // Hkv >= 8)
+    assert kern.startswith("decode_mfma") == (Hq // Hkv >= 4)
 
 
 def test_gqa_decode_full_size_sampled():
