@@ -214,7 +214,7 @@ size_t attn_bwd_workspace_bytes(int B, int H, int Tq);
  * fp32 accumulation; P and dS are rounded to bf16 as MFMA operands.
  * Errors: as attn_fwd, plus ATTN_EINVAL for NULL dout/lse/dq/dk/dv or
  * overlapping buffers, ATTN_EWORKSPACE for a missing or small workspace.
- * Supported: d = 64.
+ * Supported: d in {64, 128}.
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
              float* dq, float* dk, float* dv, int B, int H, int Tq, int Tkv, int d, int causal, float scale,

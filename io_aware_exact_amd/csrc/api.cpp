@@ -263,7 +263,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
     if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
         return fail(ATTN_EINVAL, "dout, dq, dk and dv must be 16-byte aligned");
     if (!aligned(lse, 4)) return fail(ATTN_EINVAL, "lse must be 4-byte aligned");
-    if (!attn::backward_supports(d)) return fail(ATTN_EUNSUPPORTED, "backward supports d = 64");
+    if (!attn::backward_supports(d)) return fail(ATTN_EUNSUPPORTED, "backward supports d in {64, 128}");
     if (double(Tkv) * d * 2 >= 2147483648.0 || double(Tq) * d * 2 >= 2147483648.0)
         return fail(ATTN_EUNSUPPORTED, "backward supports T*d*2 < 2^31 bytes per head");
     if (double(B) * H * ((std::max(Tq, Tkv) + 127) / 128) > 2147483647.0) return fail(ATTN_EINVAL, "grid too large");

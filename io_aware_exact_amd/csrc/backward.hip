@@ -1,4 +1,4 @@
-// Exact attention backward, bf16 inputs, head width 64, gfx950.
+// Exact attention backward, bf16 inputs, head width 64 or 128, gfx950.
 //
 // The softmax output is not stored by the forward pass; it is recomputed here
 // from Q, K, V and the saved per-row log-sum-exp ("IO-Aware Attention:
@@ -15,63 +15,100 @@
 // * bwd_stats: per query row (lse2, D) -- one streaming pass over O and dO.
 // * bwd_dkdv: one workgroup per 128-key tile (32 keys per wave, one key per
 //   lane column).  K and V of the wave stay in VGPRs as MFMA B operands; Q and
-//   dO blocks of 64 rows and their row statistics stream through a 3-stage
-//   LDS ring filled by DMA.  Per block: S = Q K^T and dP = dO V^T (Q, dO read
+//   dO blocks (64 rows at d = 64, 32 at d = 128) and their row statistics
+//   stream through a 3-stage LDS ring filled by DMA.  Per block: S = Q K^T and dP = dO V^T (Q, dO read
 //   as rows), then dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T read by
 //   ds_read_b64_tr_b16, so P and dS go from the accumulator layout to the B
 //   operand with only a bf16 pack.
 // * bwd_dq: one workgroup per 128-query tile, the forward's layout (one query
-//   per lane): S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T with K^T read
-//   transposed from the ring.
+//   per lane, key blocks of 64 at d = 64, 32 at d = 128): S^T = K Q^T,
+//   dP^T = V dO^T, dQ^T += K^T dS^T with K^T read transposed from the ring.
 // Q and dO (in bwd_dkdv) and K (in bwd_dq) are read both as rows and
 // transposed, so their LDS chunk swizzle is conflict-free for both patterns.
 // Products are bf16 MFMA with fp32 accumulation; P and dS are rounded to
 // bf16 (nearest even) as MFMA operands; dQ, dK, dV are written in fp32.
+#include <cstdio>
+
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace attn {
 namespace {
 
-constexpr int D = 64;
-constexpr int ROWB = D * 2;       // bytes per row
-constexpr int TQ = D / 16;        // k-steps over d
-constexpr int DT = D / 32;        // 32-column tiles over d
-
-// One swizzle for 128-byte rows read both ways: 16 consecutive rows map
-// their chunk c to 8 distinct chunks x 2 bank halves (row reads of 32 rows x
-// one chunk pair), and rows r, r+1 vs r+2, r+3 land in different 64-byte
-// halves (transposed reads of 8 rows x 64 bytes).
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) & 7) ^ (((row >> 1) & 1) << 2); }
+// Geometry per head width.  The chunk swizzle serves rows read both ways:
+// a row read (32 rows x one 16-byte chunk pair per instruction) and a
+// transposed read (8 rows x 64 bytes) both touch every LDS bank equally.
+// d = 64 (128-byte rows): 16 consecutive rows map a chunk to 8 distinct chunks
+// x 2 bank halves, rows r, r+1 vs r+2, r+3 land in different 64-byte halves.
+// d = 128 (256-byte rows): 16 consecutive rows map a chunk to 16 distinct
+// chunks, rows r..r+3 to 4 distinct 64-byte segments.  In both, rows r and
+// r + 16 share a swizzle and rows r and r + 8 do not.
+template <int D>
+struct BwdGeo;
+template <>
+struct BwdGeo<64> {
+    static constexpr int BQ2 = 64;   // dK/dV kernel: query rows per streamed block
+    static constexpr int BK = 64;    // dQ kernel: keys per streamed block
+    static constexpr int KV_MINW = 2;
+    static __device__ __forceinline__ int swz(int row) { return ((row >> 1) & 7) ^ (((row >> 1) & 1) << 2); }
+};
+template <>
+struct BwdGeo<128> {
+    static constexpr int BQ2 = 32;
+    static constexpr int BK = 32;
+    static constexpr int KV_MINW = 1;   // K, V and both accumulators: 192 registers before any temporary
+    static __device__ __forceinline__ int swz(int row) { return (row & 15) ^ ((row & 3) << 2); }
+};
 
 // Byte offset of the 8-byte piece holding columns col..col+3 of a swizzled row.
+template <int D>
 __device__ __forceinline__ uint32_t tr_off(int row, int col) {
-    return (uint32_t)(row * ROWB + ((((col >> 3) ^ swz(row)) << 4) | ((col & 4) << 1)));
+    return (uint32_t)(row * D * 2 + ((((col >> 3) ^ BwdGeo<D>::swz(row)) << 4) | ((col & 4) << 1)));
 }
 
-// Four transposed reads for the 16-row k-step STP of a 32-row group at byte
-// `base`: the two 32-column tiles, rows 16 STP + (0..7) and + 8.  Rows r and
+// Transposed reads for the 16-row k-step STP of a 32-row group at byte
+// `base`: every 32-column tile, rows 16 STP + (0..7) and + 8.  Rows r and
 // r + 8 differ in their swizzle, rows r and r + 16 do not, so each tile keeps
 // one offset per 8-row half and the k-step is an immediate.
-template <int STP>
-__device__ __forceinline__ void tr_kstep(uint32_t base, const uint32_t (&o)[DT][2], u32x4_t& a0, u32x4_t& a1) {
-    u32x2_t l0 = lds_read_tr16_b64<STP * 16 * ROWB>(base + o[0][0]);
-    u32x2_t h0 = lds_read_tr16_b64<STP * 16 * ROWB>(base + o[0][1]);
-    u32x2_t l1 = lds_read_tr16_b64<STP * 16 * ROWB>(base + o[1][0]);
-    u32x2_t h1 = lds_read_tr16_b64<STP * 16 * ROWB>(base + o[1][1]);
-    lgkm_wait_4(l0, h0, l1, h1);
-    a0 = u32x4_t{l0[0], l0[1], h0[0], h0[1]};
-    a1 = u32x4_t{l1[0], l1[1], h1[0], h1[1]};
+template <int D, int STP>
+__device__ __forceinline__ void tr_kstep(uint32_t base, const uint32_t (&o)[D / 32][2], u32x4_t (&a)[D / 32]) {
+    constexpr int OFF = STP * 16 * D * 2;
+#pragma unroll
+    for (int d2 = 0; d2 < D / 32; d2 += 2) {
+        u32x2_t l0 = lds_read_tr16_b64<OFF>(base + o[d2][0]);
+        u32x2_t h0 = lds_read_tr16_b64<OFF>(base + o[d2][1]);
+        u32x2_t l1 = lds_read_tr16_b64<OFF>(base + o[d2 + 1][0]);
+        u32x2_t h1 = lds_read_tr16_b64<OFF>(base + o[d2 + 1][1]);
+        lgkm_wait_4(l0, h0, l1, h1);
+        a[d2] = u32x4_t{l0[0], l0[1], h0[0], h0[1]};
+        a[d2 + 1] = u32x4_t{l1[0], l1[1], h1[0], h1[1]};
+    }
+}
+
+// Transposed-read offsets of a lane: lane group lg = lane / 16, jj = lane % 16
+// addresses row 4(lg/2) + jj/4 (and + 8), columns 32dt + 16(lg%2) + 4(jj%4).
+template <int D>
+__device__ __forceinline__ void tr_offsets(int lane, uint32_t (&o)[D / 32][2]) {
+    const int lg = lane >> 4, jj = lane & 15;
+    const int row = 4 * (lg >> 1) + (jj >> 2);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+        const int col = 32 * dt + 16 * (lg & 1) + 4 * (jj & 3);
+        o[dt][0] = tr_off<D>(row, col);
+        o[dt][1] = tr_off<D>(row + 8, col);
+    }
 }
 
 // ---------------------------------------------------------------- statistics
 
-// stats[bh * Tq + i] = (lse_i * log2 e, sum_d dO_id O_id); 8 lanes per row.
+// stats[bh * Tq + i] = (lse_i * log2 e, sum_d dO_id O_id); D/8 lanes per row.
+template <int D>
 __global__ __launch_bounds__(256)
 void bwd_stats_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
                       const float* __restrict__ LSE, float2* __restrict__ stats, long long rows) {
-    const long long r = (long long)blockIdx.x * 32 + (threadIdx.x >> 3);
-    const int part = threadIdx.x & 7;
+    constexpr int LPR = D / 8;
+    const long long r = (long long)blockIdx.x * (256 / LPR) + (threadIdx.x / LPR);
+    const int part = threadIdx.x % LPR;
     float acc = 0.f;
     if (r < rows) {
         const u32x4_t o = *reinterpret_cast<const u32x4_t*>(O + r * D + 8 * part);
@@ -82,7 +119,7 @@ void bwd_stats_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict
             acc = __builtin_fmaf(bf16_hi(o[i]), bf16_hi(g[i]), acc);
         }
     }
-    acc = group_sum<8>(acc);
+    acc = group_sum<LPR>(acc);
     if (r < rows && part == 0) stats[r] = make_float2(LSE[r] * 1.44269504088896340736f, acc);
 }
 
@@ -90,18 +127,26 @@ void bwd_stats_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict
 
 constexpr int KV_WAVES = 4;
 constexpr int BKV = 32 * KV_WAVES;   // keys per workgroup
-constexpr int BQ2 = 64;              // query rows per streamed block
 constexpr int NS = 3;                // ring stages
-constexpr int QBLK = BQ2 * ROWB;     // 8 KiB
-constexpr int STAGE = 2 * QBLK + 1024;
-constexpr int KV_LI = QBLK / 1024 / KV_WAVES;   // DMA instructions per wave per operand per block
 
-template <bool CAUSAL>
-__global__ __launch_bounds__(KV_WAVES * 64, 2)
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(KV_WAVES * 64, BwdGeo<D>::KV_MINW)
 void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                      const float2* __restrict__ stats, float* __restrict__ dK, float* __restrict__ dV,
                      int Tq, int Tkv, int BH, int nkt, float c, float scale) {
+    using G = BwdGeo<D>;
+    constexpr int ROWB = D * 2;
+    constexpr int TQ = D / 16;
+    constexpr int DT = D / 32;
+    constexpr int CPR = ROWB / 16;
+    constexpr int RPG = 1024 / ROWB;
+    constexpr int BQ2 = G::BQ2;
+    constexpr int NSUB = BQ2 / 32;           // 32-row sub-tiles per block
+    constexpr int QBLK = BQ2 * ROWB;         // 8 KiB
+    constexpr int STAGE = 2 * QBLK + 1024;
+    constexpr int KV_LI = QBLK / 1024 / KV_WAVES;
+    static_assert(KV_LI * KV_WAVES * 1024 == QBLK, "block rows must split evenly over the waves");
     __shared__ __attribute__((aligned(1024))) uint8_t ring[NS][STAGE];
 
     const int tid = threadIdx.x;
@@ -147,14 +192,14 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     qb_free = max(qb_free, qb_first);
     const int qb_full_end = Tq / BQ2;             // blocks before this have no ragged rows
 
-    // DMA: wave w moves row groups g = w + 4i (8 rows = 1 KiB) of Q and dO,
-    // and every wave moves the block's 512 bytes of row statistics
+    // DMA: wave w moves row groups g = w + 4i (1 KiB) of Q and dO, and every
+    // wave moves the block's row statistics (BQ2 * 8 bytes)
     uint32_t voff[KV_LI];
 #pragma unroll
     for (int i = 0; i < KV_LI; ++i) {
         const int g = wave + KV_WAVES * i;
-        const int row = 8 * g + (lane >> 3);
-        voff[i] = (uint32_t)(row * ROWB + (((lane & 7) ^ swz(row)) << 4));
+        const int row = RPG * g + lane / CPR;
+        voff[i] = (uint32_t)(row * ROWB + (((lane % CPR) ^ G::swz(row)) << 4));
     }
     auto issue = [&](int j) {
         const bool live = j < nqb;
@@ -178,21 +223,12 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     // row-read offsets (A operand of S = Q K^T and dP = dO V^T): row ln, chunk 2t + hf
     uint32_t r_off[TQ];
 #pragma unroll
-    for (int t = 0; t < TQ; ++t) r_off[t] = (uint32_t)(ln * ROWB + (((2 * t + hf) ^ swz(ln)) << 4));
+    for (int t = 0; t < TQ; ++t) r_off[t] = (uint32_t)(ln * ROWB + (((2 * t + hf) ^ G::swz(ln)) << 4));
     // transposed-read offsets (A operand of dV^T = dO^T P, dK^T = Q^T dS): lane group
     // lg = lane / 16, jj = lane % 16 addresses row 4(lg/2) + jj/4 (+8), columns
     // 32dt + 16(lg%2) + 4(jj%4)
     uint32_t t_off[DT][2];
-    {
-        const int lg = lane >> 4, jj = lane & 15;
-        const int row = 4 * (lg >> 1) + (jj >> 2);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const int col = 32 * dt + 16 * (lg & 1) + 4 * (jj & 3);
-            t_off[dt][0] = tr_off(row, col);
-            t_off[dt][1] = tr_off(row + 8, col);
-        }
-    }
+    tr_offsets<D>(lane, t_off);
 
     f32x16_t dkt[DT], dvt[DT];
 #pragma unroll
@@ -257,13 +293,17 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
             const u32x4_t dv = {dw[4 * stp], dw[4 * stp + 1], dw[4 * stp + 2], dw[4 * stp + 3]};
             const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pv);
             const bf16x8_t db = __builtin_bit_cast(bf16x8_t, dv);
-            u32x4_t a0, a1;
-            tr_kstep<stp>(gb, t_off, a0, a1);
-            dvt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a0), pb, dvt[0], 0, 0, 0);
-            dvt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a1), pb, dvt[1], 0, 0, 0);
-            tr_kstep<stp>(qb, t_off, a0, a1);
-            dkt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a0), db, dkt[0], 0, 0, 0);
-            dkt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a1), db, dkt[1], 0, 0, 0);
+            u32x4_t a[DT];
+            tr_kstep<D, stp>(gb, t_off, a);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                dvt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[dt]), pb, dvt[dt],
+                                                                  0, 0, 0);
+            tr_kstep<D, stp>(qb, t_off, a);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                dkt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[dt]), db, dkt[dt],
+                                                                  0, 0, 0);
         };
         kstep(std::integral_constant<int, 0>{});
         kstep(std::integral_constant<int, 1>{});
@@ -278,9 +318,9 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         const uint8_t* st = &ring[j % NS][0];
         const int q0 = j * BQ2;
         const bool free_blk = (j >= qb_free) && (j < qb_full_end);
-        // one sub-tile at a time (not unrolled: the two would double the live registers)
+        // one sub-tile at a time (not unrolled: two would double the live registers)
 #pragma nounroll
-        for (int qs = 0; qs < 2; ++qs) {
+        for (int qs = 0; qs < NSUB; ++qs) {
             if (free_blk) {
                 subtile(st, q0, qs, std::false_type{});
             } else if (!CAUSAL || q0 + 32 * qs + 31 + off >= k0 + 32 * wave) {
@@ -318,16 +358,24 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 
 constexpr int DQ_WAVES = 4;
 constexpr int BQ = 32 * DQ_WAVES;   // query rows per workgroup
-constexpr int BK = 64;              // keys per streamed block
-constexpr int KBLK = BK * ROWB;     // 8 KiB
-constexpr int DQ_LI = KBLK / 1024 / DQ_WAVES;
 
-template <bool CAUSAL>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(DQ_WAVES * 64, 2)
 void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                    const float2* __restrict__ stats, float* __restrict__ dQ,
                    int Tq, int Tkv, int BH, int nqt, float c, float scale) {
+    using G = BwdGeo<D>;
+    constexpr int ROWB = D * 2;
+    constexpr int TQ = D / 16;
+    constexpr int DT = D / 32;
+    constexpr int CPR = ROWB / 16;
+    constexpr int RPG = 1024 / ROWB;
+    constexpr int BK = G::BK;            // keys per streamed block
+    constexpr int KT = BK / 32;          // 32-key tiles per block
+    constexpr int KBLK = BK * ROWB;      // 8 KiB
+    constexpr int DQ_LI = KBLK / 1024 / DQ_WAVES;
+    static_assert(DQ_LI * DQ_WAVES * 1024 == KBLK, "block rows must split evenly over the waves");
     __shared__ __attribute__((aligned(1024))) uint8_t ring[NS][2][KBLK];
 
     const int tid = threadIdx.x;
@@ -378,8 +426,8 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 #pragma unroll
     for (int i = 0; i < DQ_LI; ++i) {
         const int g = wave + DQ_WAVES * i;
-        const int row = 8 * g + (lane >> 3);
-        voff[i] = (uint32_t)(row * ROWB + (((lane & 7) ^ swz(row)) << 4));
+        const int row = RPG * g + lane / CPR;
+        voff[i] = (uint32_t)(row * ROWB + (((lane % CPR) ^ G::swz(row)) << 4));
     }
     auto issue = [&](int j) {
         const int kb = j * BK;
@@ -399,18 +447,9 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 
     uint32_t r_off[TQ];
 #pragma unroll
-    for (int t = 0; t < TQ; ++t) r_off[t] = (uint32_t)(ln * ROWB + (((2 * t + hf) ^ swz(ln)) << 4));
+    for (int t = 0; t < TQ; ++t) r_off[t] = (uint32_t)(ln * ROWB + (((2 * t + hf) ^ G::swz(ln)) << 4));
     uint32_t t_off[DT][2];
-    {
-        const int lg = lane >> 4, jj = lane & 15;
-        const int row = 4 * (lg >> 1) + (jj >> 2);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const int col = 32 * dt + 16 * (lg & 1) + 4 * (jj & 3);
-            t_off[dt][0] = tr_off(row, col);
-            t_off[dt][1] = tr_off(row + 8, col);
-        }
-    }
+    tr_offsets<D>(lane, t_off);
 
     f32x16_t dqt[DT];
 #pragma unroll
@@ -421,10 +460,10 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     auto step = [&](const uint8_t* kst, int kb, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const uint8_t* vst = kst + KBLK;
-        // S^T and dP^T for the block's 64 keys (two 32-key tiles); lane = query column
-        uint32_t dw[16];
+        // S^T and dP^T for the block's keys (KT 32-key tiles); lane = query column
+        uint32_t dw[8 * KT];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < KT; ++kt) {
             f32x16_t s, dp;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -457,15 +496,19 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
             constexpr int stp = decltype(stp_tag)::value;
             const u32x4_t dv = {dw[4 * stp], dw[4 * stp + 1], dw[4 * stp + 2], dw[4 * stp + 3]};
             const bf16x8_t db = __builtin_bit_cast(bf16x8_t, dv);
-            u32x4_t a0, a1;
-            tr_kstep<stp>(kbase, t_off, a0, a1);
-            dqt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a0), db, dqt[0], 0, 0, 0);
-            dqt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a1), db, dqt[1], 0, 0, 0);
+            u32x4_t a[DT];
+            tr_kstep<D, stp>(kbase, t_off, a);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                dqt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[dt]), db, dqt[dt],
+                                                                  0, 0, 0);
         };
         kstep(std::integral_constant<int, 0>{});
         kstep(std::integral_constant<int, 1>{});
-        kstep(std::integral_constant<int, 2>{});
-        kstep(std::integral_constant<int, 3>{});
+        if constexpr (KT > 1) {
+            kstep(std::integral_constant<int, 2>{});
+            kstep(std::integral_constant<int, 3>{});
+        }
     };
 
     const int nfull = CAUSAL ? min(Tkv / BK, (q0 + off + 1) / BK) : Tkv / BK;
@@ -504,40 +547,50 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     }
 }
 
-template <bool CAUSAL>
+template <int D, bool CAUSAL>
 hipError_t launch_bwd_c(const BackwardArgs& a, hipStream_t stream) {
     const int BHn = a.B * a.H;
     const long long rows = (long long)BHn * a.Tq;
     float2* stats = static_cast<float2*>(a.workspace);
-    hipLaunchKernelGGL(bwd_stats_kernel, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, stream,
+    constexpr int RPW = 256 / (D / 8);
+    hipLaunchKernelGGL((bwd_stats_kernel<D>), dim3((unsigned)((rows + RPW - 1) / RPW)), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout), a.lse, stats, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nkt = (a.Tkv + BKV - 1) / BKV;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<CAUSAL>), dim3((unsigned)(nkt * BHn)), dim3(KV_WAVES * 64), 0, stream,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(nkt * BHn)), dim3(KV_WAVES * 64), 0, stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), stats, a.dk, a.dv,
                        a.Tq, a.Tkv, BHn, nkt, a.c, a.scale);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int nqt = (a.Tq + BQ - 1) / BQ;
-    hipLaunchKernelGGL((bwd_dq_kernel<CAUSAL>), dim3((unsigned)(nqt * BHn)), dim3(DQ_WAVES * 64), 0, stream,
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(nqt * BHn)), dim3(DQ_WAVES * 64), 0, stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), stats, a.dq,
                        a.Tq, a.Tkv, BHn, nqt, a.c, a.scale);
     return hipGetLastError();
 }
 
+thread_local char g_name[128];
+
 }  // namespace
 
-bool backward_supports(int d) { return d == D; }
+bool backward_supports(int d) { return d == 64 || d == 128; }
 
 size_t backward_workspace_bytes(int B, int H, int Tq) { return (size_t)B * H * Tq * sizeof(float2); }
 
 hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream, const char** name) {
-    *name = a.causal ? "bwd_bf16_d64<stats+dkdv(bk=128,bq=64)+dq(bq=128,bk=64),causal>"
-                     : "bwd_bf16_d64<stats+dkdv(bk=128,bq=64)+dq(bq=128,bk=64)>";
-    if (a.causal) return launch_bwd_c<true>(a, stream);
-    return launch_bwd_c<false>(a, stream);
+    const int bq2 = a.d == 128 ? BwdGeo<128>::BQ2 : BwdGeo<64>::BQ2;
+    const int bk = a.d == 128 ? BwdGeo<128>::BK : BwdGeo<64>::BK;
+    snprintf(g_name, sizeof g_name, "bwd_bf16_d%d<stats+dkdv(bk=128,bq=%d)+dq(bq=128,bk=%d)%s>", a.d, bq2, bk,
+             a.causal ? ",causal" : "");
+    *name = g_name;
+    if (a.d == 128) {
+        if (a.causal) return launch_bwd_c<128, true>(a, stream);
+        return launch_bwd_c<128, false>(a, stream);
+    }
+    if (a.causal) return launch_bwd_c<64, true>(a, stream);
+    return launch_bwd_c<64, false>(a, stream);
 }
 
 }  // namespace attn

@@ -83,14 +83,20 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("B,H,Tq,Tkv,causal", CASES)
-def test_backward_shapes(B, H, Tq, Tkv, causal):
-    check(Workload(f"bwd[{B},{H},{Tq},{Tkv},{'c' if causal else 'n'}]", B, H, Tq, Tkv, 64, "bf16", causal,
-                   seed=200 + Tq + Tkv))
+def test_backward_shapes(B, H, Tq, Tkv, causal, d):
+    check(Workload(f"bwd[{B},{H},{Tq},{Tkv},{'c' if causal else 'n'},d={d}]", B, H, Tq, Tkv, d, "bf16", causal,
+                   seed=200 + Tq + Tkv + d))
+    assert attn.attn_last_kernel().startswith(f"bwd_bf16_d{d}<")
 
 
 def test_backward_gpt2_full():
     check(WORKLOADS["gpt2"])
+
+
+def test_backward_gpt2_shape_d128_full():
+    check(WORKLOADS["gpt2"].with_(name="gpt2_d128", d=128, seed=12))
 
 
 def test_backward_spread_scores():
