@@ -366,3 +366,56 @@ def test_no_device_allocation_during_call():
     free1, _ = torch.cuda.mem_get_info()
     # one T x T fp32 score matrix per head would be 1 GiB here
     assert free0 - free1 < (1 << 20)
+
+
+def test_prepared_calls_allocate_nothing():
+    """With outputs and workspaces preallocated, the split forward, grouped
+    decode and backward calls allocate no device memory."""
+    w = WORKLOADS["long_1head"].with_(Tq=4096, Tkv=4096)
+    q, k, v = [t.cuda() for t in make_qkv(w)]
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    ws = torch.empty(attn.attn_fwd_split_workspace_bytes(1, 1, 4096, 4096, 64, True, 0), dtype=torch.uint8,
+                     device="cuda")
+    fwd = attn.prepared_fwd(q, k, v, o, lse, True, kv_chunk=0, workspace=ws)
+    dq = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    dk, dv = torch.empty_like(dq), torch.empty_like(dq)
+    bws = torch.empty(attn.attn_bwd_workspace_bytes(1, 1, 4096), dtype=torch.uint8, device="cuda")
+    do = torch.ones_like(q)
+    bwd = attn.prepared_bwd(q, k, v, o, lse, do, dq, dk, dv, True, bws)
+    g = Workload("gqa_alloc", 2, 16, 1, 4096, 128, "bf16", False, seed=31, Hkv=2)
+    gq, gk, gv = [t.cuda() for t in make_qkv(g)]
+    go = torch.empty_like(gq)
+    glse = torch.empty((2, 16), dtype=torch.float32, device="cuda")
+    gws = torch.empty(attn.attn_decode_workspace_bytes(2, 16, 128, 8), dtype=torch.uint8, device="cuda")
+    dec = attn.prepared_decode(gq, gk, gv, go, glse, 8, gws)
+    fwd(); bwd(); dec()
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    for _ in range(3):
+        fwd(); bwd(); dec()
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert free0 - free1 < (1 << 20)
+
+
+def test_calls_run_on_the_current_stream():
+    """Every entry point enqueues on the caller's stream: results computed on a
+    side stream (default priority) equal the default stream's."""
+    w = Workload("streams", 2, 3, 300, 300, 64, "bf16", True, seed=32)
+    q, k, v = [t.cuda() for t in make_qkv(w)]
+    do = torch.ones_like(q)
+    ref_o, ref_l = attn.attn_fwd(q, k, v, causal=True)
+    ref_g = attn.attn_bwd(q, k, v, ref_o, ref_l, do, causal=True)
+    ref_d = attn.attn_decode(q[:, :, :1].contiguous(), k, v, num_splits=4)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        o, l = attn.attn_fwd(q, k, v, causal=True)
+        g = attn.attn_bwd(q, k, v, o, l, do, causal=True)
+        d = attn.attn_decode(q[:, :, :1].contiguous(), k, v, num_splits=4)
+    side.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+    for a, b in zip(g, ref_g):
+        assert torch.equal(a, b)
+    assert torch.equal(d[0], ref_d[0]) and torch.equal(d[1], ref_d[1])
