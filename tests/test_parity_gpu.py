@@ -359,6 +359,7 @@ def test_no_device_allocation_during_call():
     q, k, v = [t.cuda() for t in make_qkv(w)]
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    attn.attn_fwd(q, k, v, causal=True, out=o, lse=lse)   # the runtime's one-time set-up of a first launch
     torch.cuda.synchronize()
     free0, _ = torch.cuda.mem_get_info()
     attn.attn_fwd(q, k, v, causal=True, out=o, lse=lse)
