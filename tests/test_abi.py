@@ -229,6 +229,16 @@ def test_backward_arguments(lib):
     assert attn.attn_bwd_workspace_bytes(0, 3, 64) == 0
 
 
+def test_largest_heads_are_bounded():
+    """K/V of one head must stay under 2^31 bytes (32-bit buffer ranges)."""
+    big = (1 << 31) // (2 * 64)          # keys at d = 64 reaching exactly 2^31 bytes
+    assert fwd(lib := attn.lib(), Tkv=big, Tq=64, causal=0) == EUNSUP and "2^31" in attn.attn_status_string(EUNSUP)
+    assert fwd(lib, Tkv=big - 1, Tq=64, causal=0, q=0) == EINVAL    # the size itself is accepted (fails on q)
+    assert fsplit(lib, B=1, H=1, Tkv=big, Tq=64, causal=0) == EUNSUP
+    assert dec(lib, B=1, H=1, Tkv=(1 << 31) // 256) == EUNSUP
+    assert bwd(lib, B=1, H=1, Tkv=big, causal=0) == EUNSUP
+
+
 def test_workspace_size_formula():
     assert attn.attn_decode_workspace_bytes(64, 32, 128, 16) == 64 * 32 * 16 * 130 * 4
     assert attn.attn_decode_workspace_bytes(1, 1, 64, 1) == 0

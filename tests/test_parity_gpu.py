@@ -8,6 +8,7 @@ the full-size workloads compare sampled rows the oracle computes one by one,
 in the same launch configuration the benchmark times.
 """
 
+import math
 import sys
 
 import numpy as np
@@ -420,3 +421,37 @@ def test_calls_run_on_the_current_stream():
     for a, b in zip(g, ref_g):
         assert torch.equal(a, b)
     assert torch.equal(d[0], ref_d[0]) and torch.equal(d[1], ref_d[1])
+
+
+
+@pytest.mark.parametrize("api", ["decode", "prefill_split"])
+def test_longest_accepted_head(api):
+    """One head of 8,388,607 keys at d = 128 (K and V 2 GiB each, the largest
+    the 32-bit buffer ranges accept), sampled rows against the oracle: the
+    oracle runs on 2^20-key partitions and merges them with its own partition
+    combine."""
+    d, T = 128, (1 << 23) - 1
+    g = torch.Generator(device="cuda").manual_seed(77)
+    k = torch.randn((1, 1, T, d), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((1, 1, T, d), generator=g, device="cuda").to(torch.bfloat16)
+    tq = 1 if api == "decode" else 130
+    q = torch.randn((1, 1, tq, d), generator=g, device="cuda").to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(d)
+    say(f"case {api}: T_kv={T}, T_q={tq}, d={d}")
+    if api == "decode":
+        o, lse = attn.attn_decode(q, k, v, scale=scale, num_splits=0)
+        lse = lse[:, :, None]
+    else:
+        o, lse = attn.attn_fwd_split(q, k, v, causal=False, scale=scale, kv_chunk=0)
+    torch.cuda.synchronize()
+    say(f"  kernel {attn.attn_last_kernel()}")
+    rows = sorted({0, tq - 1})
+    qr = to_f64(q[:, :, rows])
+    kh, vh = k.cpu(), v.cpu()
+    parts = [oracle.attention(qr, to_f64(kh[:, :, i:i + (1 << 20)]), to_f64(vh[:, :, i:i + (1 << 20)]), scale)
+             for i in range(0, T, 1 << 20)]
+    o_ref, lse_ref = oracle.combine_partials(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    eo = float(np.abs(to_f64(o[:, :, rows]) - o_ref).max())
+    el = float(np.abs(to_f64(lse[:, :, rows]) - lse_ref).max())
+    say(f"  max|dO|={eo:.2e} max|dLSE|={el:.2e}")
+    assert eo <= 2e-2 and el <= 1e-3
