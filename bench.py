@@ -33,6 +33,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -74,11 +75,17 @@ def decode_bytes(w) -> tuple[int, int]:
 
 
 def kernel_sources_digest() -> str:
+    """Digest of the library sources with comments and whitespace removed, so
+    that only a change to the code itself invalidates recorded counters."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "io_aware_exact_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        text = " ".join(text.split())
+        h.update(f.encode() + b"\0" + text.encode())
     return h.hexdigest()[:16]
 
 

@@ -51,6 +51,9 @@
 // * Tiles are launched heaviest-first (last query tiles first) and the
 //   linear block id keeps every tile of one (batch, head) on one XCD when the
 //   number of heads is a multiple of 8.
+// * Grids of too few 128-row tiles (d = 64) use 64-row tiles whose key loop
+//   is split over the two waves of a pair and merged through LDS at the end
+//   (KS = 2 below), which halves the serial chain of the heaviest tiles.
 #include <cstdio>
 
 #include "common.hpp"
@@ -101,23 +104,33 @@ __host__ __device__ __forceinline__ int tile_chunks(int nblk, int chunk) {
 // Units of unsplit tiles write O and LSE; units of split tiles write their
 // partial result (O normalised by the chunk's own sum, and the chunk's
 // base-2 log-sum-exp) to `part`, merged later by prefill_combine_kernel.
-template <int D, int WAVES, int NS, bool CAUSAL>
+//
+// KS = 2 (key halves, d = 64 only): the waves form WAVES/2 query row groups of
+// 32 rows, and each row group has two waves that take the two 32-key halves of
+// every 64-key stage; the pair merges its two (m, l, O) states through LDS at
+// the end with the same rescaling.  Tiles are then BQ = 64 rows and the serial
+// key loop of a tile is half as long, for shapes with too few 128-row tiles
+// to fill the chip (no workspace, no second kernel).
+template <int D, int WAVES, int NS, bool CAUSAL, int KS = 1>
 __global__ __launch_bounds__(WAVES * 64, 2)
 void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                          const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                          float* __restrict__ LSE, float* __restrict__ part, int Tq, int Tkv, int BH,
                          int nqt, int chunk, int nch_max, float c) {
     using G = Geo<D>;
-    constexpr int BK = G::BK;
-    constexpr int BQ = WAVES * 32;
+    static_assert(KS == 1 || (KS == 2 && D == 64 && WAVES % 2 == 0), "key halves need 64-key stages");
+    constexpr int BK = G::BK;                 // keys per ring stage
+    constexpr int WK = BK / KS;               // keys per wave per stage
+    constexpr int RG = WAVES / KS;            // query row groups of 32 rows
+    constexpr int BQ = RG * 32;
     constexpr int ROWB = D * 2;               // bytes per K/V row
     constexpr int TILEB = BK * ROWB;          // bytes per K (or V) block: 8 KiB
     constexpr int CPR = ROWB / 16;            // 16-byte chunks per row
     constexpr int RPG = 1024 / ROWB;          // rows per 1 KiB load instruction
     constexpr int TQ = D / 16;                // k-steps of the QK product
     constexpr int DT = D / 32;                // 32-column tiles of O
-    constexpr int KT = BK / 32;               // 32-key tiles of S
-    constexpr int ST = BK / 16;               // 16-key steps of the PV product
+    constexpr int KT = WK / 32;               // 32-key tiles of S
+    constexpr int ST = WK / 16;               // 16-key steps of the PV product
     static_assert((TILEB / 1024) % WAVES == 0, "row groups of a block must split evenly over the waves");
     constexpr int LI = TILEB / 1024 / WAVES;  // 1 KiB load instructions per wave per operand per block
 
@@ -128,15 +141,33 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     const int wave = tid >> 6;
     const int ln = lane & 31;
     const int hf = lane >> 5;
+    const int rg = wave % RG;                 // query row group
+    const int kh = wave / RG;                 // key half of every stage (KS = 2)
 
     // unit id = (cc * nqt + rank) * BH + bh: first chunks of every tile first,
     // heaviest tiles first within a chunk index, and all units of one
-    // (batch, head) on one XCD when BH is a multiple of 8
+    // (batch, head) on one XCD when BH is a multiple of 8.
+    // Causal key halves with at least three rounds of 32 units per XCD (one
+    // per compute unit per round, three resident per compute unit): the
+    // second round runs light-to-heavy (a snake over the heaviest-first
+    // order), so the units that share a compute unit sum to similar work.
     const int id = blockIdx.x;
-    const int bh = id % BH;
-    const int rest = id / BH;
-    const int rank = rest % nqt;
-    const int cc = rest / nqt;
+    int bh, rank, cc;
+    if (CAUSAL && KS == 2 && BH % 8 == 0 && nqt * (BH >> 3) >= 96) {
+        const int xcd = id & 7, k = id >> 3;        // k-th unit of this XCD
+        const int per = BH >> 3;                    // heads per XCD
+        const int round = k / 32, pos = k % 32;
+        const bool full = (round + 1) * 32 <= nqt * per;
+        const int p = ((round & 1) && full) ? round * 32 + 31 - pos : k;
+        rank = p / per;
+        bh = (p % per) * 8 + xcd;
+        cc = 0;
+    } else {
+        bh = id % BH;
+        const int rest = id / BH;
+        rank = rest % nqt;
+        cc = rest / nqt;
+    }
     const int qt = CAUSAL ? (nqt - 1 - rank) : rank;
     const int q0 = qt * BQ;
     const int off = Tkv - Tq;                 // bottom-right causal alignment
@@ -152,8 +183,8 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     const uint16_t* Kh = K + kvbase;
     const uint16_t* Vh = V + kvbase;
 
-    // ---- Q fragment: row q0 + 32*wave + ln, d = 16t + 8hf + (0..7) ----
-    const int qrow = q0 + wave * 32 + ln;
+    // ---- Q fragment: row q0 + 32*rg + ln, d = 16t + 8hf + (0..7) ----
+    const int qrow = q0 + rg * 32 + ln;
     bf16x8_t qf[TQ];
     if (qrow < Tq) {
         const u32x4_t* src = reinterpret_cast<const u32x4_t*>(Q + qbase + (size_t)qrow * D + 8 * hf);
@@ -164,7 +195,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
         for (int t = 0; t < TQ; ++t) qf[t] = __builtin_bit_cast(bf16x8_t, u32x4_t{0, 0, 0, 0});
     }
 
-    const int wq_first = q0 + wave * 32;       // this wave's first / last query row
+    const int wq_first = q0 + rg * 32;         // this wave's first / last query row
     const int wq_last = wq_first + 31;
     const int lim = CAUSAL ? min(Tkv - 1, qrow + off) : (Tkv - 1);   // last key this row may see
 
@@ -238,6 +269,26 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
                 s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kt], 0, 0, 0);
             }
         }
+        // With key halves the V operand of the whole half-block fits in
+        // registers: its LDS reads are issued here, before the softmax, and
+        // their latency hides under it instead of sitting between the
+        // softmax and the PV product.
+        const uint32_t vbase = lds_addr(vst);
+        constexpr bool HOIST_V = (KS == 2);
+        [[maybe_unused]] u32x2_t vr[ST][DT][2];
+        if constexpr (HOIST_V) {
+            static_assert(ST == 2 && DT == 2, "hoisted V reads assume one 32-key, 64-column half-block");
+            __builtin_amdgcn_sched_barrier(0);    // after every QK MFMA has issued
+            vr[0][0][0] = lds_read_tr16_b64<0>(vbase + v_roff[0]);
+            vr[0][0][1] = lds_read_tr16_b64<8 * ROWB>(vbase + v_roff[0]);
+            vr[0][1][0] = lds_read_tr16_b64<0>(vbase + v_roff[1]);
+            vr[0][1][1] = lds_read_tr16_b64<8 * ROWB>(vbase + v_roff[1]);
+            vr[1][0][0] = lds_read_tr16_b64<16 * ROWB>(vbase + v_roff[0]);
+            vr[1][0][1] = lds_read_tr16_b64<24 * ROWB>(vbase + v_roff[0]);
+            vr[1][1][0] = lds_read_tr16_b64<16 * ROWB>(vbase + v_roff[1]);
+            vr[1][1][1] = lds_read_tr16_b64<24 * ROWB>(vbase + v_roff[1]);
+            __builtin_amdgcn_sched_barrier(0);    // ... and before the softmax
+        }
         if constexpr (MASK) {
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
@@ -283,7 +334,22 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
             exponentiate(m_use);
         }
         l += rs;
-        const uint32_t vbase = lds_addr(vst);
+        if constexpr (HOIST_V) {
+            lgkm_wait_4(vr[0][0][0], vr[0][0][1], vr[0][1][0], vr[0][1][1]);
+            lgkm_wait_4(vr[1][0][0], vr[1][0][1], vr[1][1][0], vr[1][1][1]);
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const u32x4_t pv = {pw[4 * st], pw[4 * st + 1], pw[4 * st + 2], pw[4 * st + 3]};
+                const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pv);
+#pragma unroll
+                for (int dt = 0; dt < 2; ++dt) {
+                    const u32x4_t a = {vr[st][dt][0][0], vr[st][dt][0][1], vr[st][dt][1][0], vr[st][dt][1][1]};
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), pb,
+                                                                       oacc[dt], 0, 0, 0);
+                }
+            }
+            return;
+        }
         auto pv_step = [&](auto st_tag) {
             constexpr int st = decltype(st_tag)::value;
             constexpr int o = st * 16 * ROWB;
@@ -323,20 +389,54 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
 
     int j = jlo;
     const int jfull = min(nfull, jhi);
+    // this wave's keys of a stage: rows [kh*WK, kh*WK + WK)
+    constexpr int HALF = WK * ROWB;
     for (; j < jfull; ++j) {
         wait_vmcnt<2 * LI * (NS - 2)>();      // this wave's part of block j has landed
         __syncthreads();                      // ... everyone's, and stage (j-1) % NS is free
         issue(j + NS - 1);
-        step(&ring[j % NS][0][0], j * BK, std::false_type{});
+        step(&ring[j % NS][0][0] + kh * HALF, j * BK + kh * WK, std::false_type{});
     }
     for (; j < jhi; ++j) {
         wait_vmcnt<2 * LI * (NS - 2)>();
         __syncthreads();
         issue(j + NS - 1);
-        const int kb = j * BK;
-        if (!CAUSAL || kb <= wq_last + off) step(&ring[j % NS][0][0], kb, std::true_type{});
+        const int kb = j * BK + kh * WK;
+        if (!CAUSAL || kb <= wq_last + off) step(&ring[j % NS][0][0] + kh * HALF, kb, std::true_type{});
     }
     wait_vmcnt<0>();    // no DMA may still be writing LDS when the workgroup retires
+
+    if constexpr (KS == 2) {
+        // The second wave of each row group hands (O, m, l) to the first
+        // through the ring (same lane layout on both sides: lane-major,
+        // conflict-free); the first merges with the rescaling merge:
+        // M = max(m_a, m_b), O = 2^(m_a-M) O_a + 2^(m_b-M) O_b, likewise l.
+        constexpr int NREG = DT * 16 + 2;
+        static_assert(RG * NREG * 64 * 4 <= NS * 2 * TILEB, "merge buffer must fit in the ring");
+        __syncthreads();                      // every wave is done reading the ring
+        float* xb = reinterpret_cast<float*>(&ring[0][0][0]) + rg * NREG * 64 + lane;
+        if (kh == 1) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) xb[(dt * 16 + r) * 64] = oacc[dt][r];
+            xb[DT * 16 * 64] = m;
+            xb[(DT * 16 + 1) * 64] = l;
+        }
+        __syncthreads();
+        if (kh == 1) return;
+        const float mb = xb[DT * 16 * 64];
+        const float lb = xb[(DT * 16 + 1) * 64];
+        const float mm = fmaxf(m, mb);
+        const float mu = (mm == kNegInf) ? 0.f : mm;
+        const float wa = fast_exp2(m - mu), wb = fast_exp2(mb - mu);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[dt][r] = wa * oacc[dt][r] + wb * xb[(dt * 16 + r) * 64];
+        l = wa * l + wb * lb;
+        m = mm;
+    }
 
     // ---- epilogue: divide once, write O (bf16) and LSE (fp32) ----
     const float lsum = half_swap_sum(l);
@@ -447,6 +547,29 @@ void prefill_combine_kernel(const float* __restrict__ part, uint16_t* __restrict
 constexpr int kWaves = 4;
 constexpr int kStages = 3;
 constexpr int kBQ = kWaves * 32;
+constexpr int kBQHalves = kWaves / 2 * 32;   // tile rows of the key-halves variant
+
+// The key-halves variant (d = 64, unsplit) takes over when the 128-row tiles
+// would leave the chip short of work: fewer than three resident tiles per
+// compute unit.
+bool use_key_halves(const PrefillArgs& a, int nch_max) {
+    if (a.d != 64 || nch_max > 1) return false;
+    const long long tiles = (long long)((a.Tq + kBQ - 1) / kBQ) * a.B * a.H;
+    return tiles < 3LL * 256;
+}
+
+template <bool CAUSAL>
+hipError_t launch_halves(const PrefillArgs& a, hipStream_t stream) {
+    const int nqt = (a.Tq + kBQHalves - 1) / kBQHalves;
+    const long long grid = (long long)nqt * a.B * a.H;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((prefill_bf16_kernel<64, kWaves, kStages, CAUSAL, 2>), dim3((unsigned)grid),
+                       dim3(kWaves * 64), 0, stream, static_cast<const uint16_t*>(a.q),
+                       static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
+                       static_cast<uint16_t*>(a.o), a.lse, static_cast<float*>(nullptr), a.Tq, a.Tkv, a.B * a.H,
+                       nqt, 0, 1, a.c);
+    return hipGetLastError();
+}
 
 template <int D, bool CAUSAL>
 hipError_t launch_one(const PrefillArgs& a, int chunk, int nch_max, hipStream_t stream) {
@@ -520,6 +643,12 @@ PrefillSplit prefill_bf16_split_plan(int B, int H, int Tq, int Tkv, int d, bool 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, const PrefillSplit& sp, hipStream_t stream,
                                const char** name) {
     const int bk = block_keys(a.d);
+    if (use_key_halves(a, sp.nch_max)) {
+        snprintf(g_name, sizeof g_name, "prefill_bf16_d64<waves=4,bq=%d,bk=64,key_halves=2,stages=3%s>", kBQHalves,
+                 a.causal ? ",causal" : "");
+        *name = g_name;
+        return a.causal ? launch_halves<true>(a, stream) : launch_halves<false>(a, stream);
+    }
     if (sp.nch_max > 1)
         snprintf(g_name, sizeof g_name, "prefill_bf16_d%d<waves=4,bq=128,bk=%d,stages=3%s,kv_chunk=%d>+combine",
                  a.d, bk, a.causal ? ",causal" : "", sp.chunk * bk);

@@ -151,6 +151,30 @@ def test_prefill_bf16_shapes(B, H, Tq, Tkv, causal, d):
         assert attn.attn_last_kernel().startswith(f"prefill_bf16_d{d}<")
 
 
+# d = 64 has two kernels: 128-row tiles, and 64-row tiles whose key loop is
+# split over two waves ("key_halves") when the 128-row tiles would number
+# fewer than 768.  Both are exercised here with ragged ends and offsets; the
+# key-halves cases with 48 heads also take its balanced (snake) unit order,
+# one of them with a partial last round.
+D64_PATH_CASES = [
+    # B, H, Tq, Tkv, causal, key halves
+    (8, 96, 129, 129, True, False),
+    (8, 96, 100, 300, True, False),
+    (4, 192, 200, 200, False, False),
+    (4, 12, 1000, 1000, True, True),
+    (2, 24, 1100, 1300, True, True),
+    (3, 5, 333, 333, False, True),
+    (1, 1, 65, 65, True, True),
+]
+
+
+@pytest.mark.parametrize("B,H,Tq,Tkv,causal,halves", D64_PATH_CASES)
+def test_prefill_bf16_d64_paths(B, H, Tq, Tkv, causal, halves):
+    full_check(Workload(f"bf16[{B},{H},{Tq},{Tkv},{'c' if causal else 'n'},d=64]", B, H, Tq, Tkv, 64, "bf16",
+                        causal, seed=3 + B * H + Tq))
+    assert ("key_halves=2" in attn.attn_last_kernel()) == halves
+
+
 @pytest.mark.parametrize("d", [16, 32, 64, 128])
 @pytest.mark.parametrize("Tq,Tkv,causal", [(256, 256, False), (100, 100, True), (70, 333, True), (1, 65, False)])
 def test_prefill_fp32_shapes(d, Tq, Tkv, causal):
