@@ -64,6 +64,13 @@ namespace {
 
 constexpr float kSumLimit = 65536.0f;         // 2^16: largest block row sum kept without raising m
 
+// A 16-byte LDS load at an LDS byte address plus a constant (the constant
+// lands in the instruction's offset field); the compiler tracks its wait.
+template <int OFF>
+__device__ __forceinline__ bf16x8_t lds_load_b128(uint32_t addr) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>((uintptr_t)(addr + OFF));
+}
+
 // Tile geometry per head width.  Rows are D*2 bytes; LDS chunk swizzles
 // (16-byte chunk index within a row) make the K operand reads (ds_read_b128,
 // 32 rows x one chunk pair per instruction) and the V transposed reads (8
@@ -138,7 +145,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int ln = lane & 31;
     const int hf = lane >> 5;
     const int rg = wave % RG;                 // query row group
@@ -269,26 +276,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
                 s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kt], 0, 0, 0);
             }
         }
-        // With key halves the V operand of the whole half-block fits in
-        // registers: its LDS reads are issued here, before the softmax, and
-        // their latency hides under it instead of sitting between the
-        // softmax and the PV product.
         const uint32_t vbase = lds_addr(vst);
-        constexpr bool HOIST_V = (KS == 2);
-        [[maybe_unused]] u32x2_t vr[ST][DT][2];
-        if constexpr (HOIST_V) {
-            static_assert(ST == 2 && DT == 2, "hoisted V reads assume one 32-key, 64-column half-block");
-            __builtin_amdgcn_sched_barrier(0);    // after every QK MFMA has issued
-            vr[0][0][0] = lds_read_tr16_b64<0>(vbase + v_roff[0]);
-            vr[0][0][1] = lds_read_tr16_b64<8 * ROWB>(vbase + v_roff[0]);
-            vr[0][1][0] = lds_read_tr16_b64<0>(vbase + v_roff[1]);
-            vr[0][1][1] = lds_read_tr16_b64<8 * ROWB>(vbase + v_roff[1]);
-            vr[1][0][0] = lds_read_tr16_b64<16 * ROWB>(vbase + v_roff[0]);
-            vr[1][0][1] = lds_read_tr16_b64<24 * ROWB>(vbase + v_roff[0]);
-            vr[1][1][0] = lds_read_tr16_b64<16 * ROWB>(vbase + v_roff[1]);
-            vr[1][1][1] = lds_read_tr16_b64<24 * ROWB>(vbase + v_roff[1]);
-            __builtin_amdgcn_sched_barrier(0);    // ... and before the softmax
-        }
         if constexpr (MASK) {
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
@@ -334,22 +322,6 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
             exponentiate(m_use);
         }
         l += rs;
-        if constexpr (HOIST_V) {
-            lgkm_wait_4(vr[0][0][0], vr[0][0][1], vr[0][1][0], vr[0][1][1]);
-            lgkm_wait_4(vr[1][0][0], vr[1][0][1], vr[1][1][0], vr[1][1][1]);
-#pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                const u32x4_t pv = {pw[4 * st], pw[4 * st + 1], pw[4 * st + 2], pw[4 * st + 3]};
-                const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pv);
-#pragma unroll
-                for (int dt = 0; dt < 2; ++dt) {
-                    const u32x4_t a = {vr[st][dt][0][0], vr[st][dt][0][1], vr[st][dt][1][0], vr[st][dt][1][1]};
-                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), pb,
-                                                                       oacc[dt], 0, 0, 0);
-                }
-            }
-            return;
-        }
         auto pv_step = [&](auto st_tag) {
             constexpr int st = decltype(st_tag)::value;
             constexpr int o = st * 16 * ROWB;
@@ -384,25 +356,199 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     // wave whose rows all precede them, skipped.
     const int nfull = CAUSAL ? min(Tkv / BK, (q0 + off + 1) / BK) : Tkv / BK;
 
+    if constexpr (KS == 2) {
+        // Software-pipelined key loop: iteration j runs the QK product of
+        // block j+1 on the matrix cores while the VALU does the softmax of
+        // block j, then the PV product of block j.  K of block b lives in
+        // ring[b % NS][0] and V in ring[b % NS][1]; K runs one block ahead of
+        // V, so iteration j issues K(j+NS) and V(j+NS-1), each into the stage
+        // the previous iteration finished with, and every operand is still
+        // requested NS-1 iterations before its use.  The interior loop is
+        // unrolled by 2*NS so that stage indices are compile-time constants
+        // (immediate LDS offsets) and the two score buffers alternate without
+        // copies.  Units are unsplit here (jlo = 0).
+        static_assert(NS == 2 || NS == 3, "2- or 3-stage ring");
+        constexpr int U = NS == 2 ? 2 : 6;   // unroll: stages and score buffers both repeat
+        constexpr int HALF = WK * ROWB;
+        constexpr int STAGEB = 2 * TILEB;     // bytes per ring stage (K + V)
+        const uint32_t ring0 = lds_addr(&ring[0][0][0]) + (uint32_t)(kh * HALF);
+        uint32_t k_ra[TQ], v_ra[DT];          // per-lane LDS read addresses in stage 0
+#pragma unroll
+        for (int t = 0; t < TQ; ++t) k_ra[t] = ring0 + k_roff[t];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) v_ra[dt] = ring0 + TILEB + v_roff[dt];
+        // DMA of block b into stage S: the descriptor covers block b to the
+        // end of the head (empty past the end: no memory traffic, and its
+        // base is then never dereferenced)
+        auto issue_blk = [&](int b, auto stage_tag, auto which_tag) {
+            constexpr int S = decltype(stage_tag)::value;
+            constexpr int W = decltype(which_tag)::value;
+            const uint32_t kb = (uint32_t)b * BK;
+            const uint32_t bytes = (uint32_t)max(Tkv - (int)kb, 0) * (uint32_t)ROWB;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc((W ? Vh : Kh) + (size_t)kb * D, bytes);
+            uint8_t* st = &ring[S][W][0];
+#pragma unroll
+            for (int i = 0; i < LI; ++i) {
+                const int g = wave + WAVES * i;
+                buffer_load_lds_b128(rs, W ? v_voff[i] : k_voff[i], st + g * 1024);
+            }
+        };
+        auto qk = [&](auto stage_tag) {
+            constexpr int S = decltype(stage_tag)::value;
+            f32x16_t acc;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+            for (int t = 0; t < TQ; ++t) {
+                const bf16x8_t a = lds_load_b128<S * STAGEB>(k_ra[t]);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], acc, 0, 0, 0);
+            }
+            return acc;
+        };
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        issue_blk(0, I0{}, I0{});
+        issue_blk(1, I1{}, I0{});
+        issue_blk(0, I0{}, I1{});
+        if constexpr (NS == 3) {
+            issue_blk(2, I2{}, I0{});
+            issue_blk(1, I1{}, I1{});
+        }
+        wait_vmcnt<2 * LI * (NS - 1)>();      // K(0) has landed
+        __syncthreads();
+        // one block j in stage S = j % 3; sc holds S of block j, nxt receives
+        // S of block j+1
+        auto body = [&](int j, f32x16_t& sc, f32x16_t& nxt, auto mask_tag, auto stage_tag) {
+            constexpr bool MASK = decltype(mask_tag)::value;
+            constexpr int S = decltype(stage_tag)::value;
+            constexpr int S1 = (S + 1) % NS, SP = (S + NS - 1) % NS;
+            wait_vmcnt<2 * LI * (NS - 2)>();  // K(j+1) and V(j) have landed (this wave's part)
+            __syncthreads();                  // ... everyone's; iteration j-1 is done everywhere
+            issue_blk(j + NS, stage_tag, I0{});                              // K(j+3) replaces K(j)
+            issue_blk(j + NS - 1, std::integral_constant<int, SP>{}, I1{});  // V(j+2) replaces V(j-1)
+            if constexpr (MASK) {
+                // diagonal / ragged block (a block this wave's rows all
+                // precede is masked whole and adds nothing)
+                const int kb = j * BK + kh * WK;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+                    if (key > lim) sc[r] = kNegInf;
+                }
+            }
+            constexpr int VO = S * STAGEB;
+            u32x2_t vr[2][2][2];
+            vr[0][0][0] = lds_read_tr16_b64<VO>(v_ra[0]);
+            vr[0][0][1] = lds_read_tr16_b64<VO + 8 * ROWB>(v_ra[0]);
+            vr[0][1][0] = lds_read_tr16_b64<VO>(v_ra[1]);
+            vr[0][1][1] = lds_read_tr16_b64<VO + 8 * ROWB>(v_ra[1]);
+            vr[1][0][0] = lds_read_tr16_b64<VO + 16 * ROWB>(v_ra[0]);
+            vr[1][0][1] = lds_read_tr16_b64<VO + 24 * ROWB>(v_ra[0]);
+            vr[1][1][0] = lds_read_tr16_b64<VO + 16 * ROWB>(v_ra[1]);
+            vr[1][1][1] = lds_read_tr16_b64<VO + 24 * ROWB>(v_ra[1]);
+            nxt = qk(std::integral_constant<int, S1>{});   // past the last block: unused
+            uint32_t pw[8];
+            float rs = 0.f;
+            auto exponentiate = [&](float mref) {
+                float p0 = fast_exp2(__builtin_fmaf(sc[0], c, -mref));
+                float p1 = fast_exp2(__builtin_fmaf(sc[1], c, -mref));
+                pw[0] = pack_bf16x2(p0, p1);
+                rs = p0 + p1;
+#pragma unroll
+                for (int i = 1; i < 8; ++i) {
+                    p0 = fast_exp2(__builtin_fmaf(sc[2 * i], c, -mref));
+                    p1 = fast_exp2(__builtin_fmaf(sc[2 * i + 1], c, -mref));
+                    pw[i] = pack_bf16x2(p0, p1);
+                    rs += p0 + p1;
+                }
+            };
+            exponentiate(m);
+            const float row = half_swap_sum(rs);
+            if (__builtin_amdgcn_ballot_w64(!(row <= kSumLimit)) != 0) {
+                float mx = kNegInf;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+                mx = half_swap_max(mx);
+                const float m_new = fmaxf(m, mx * c);
+                const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+                const float alpha = fast_exp2(m - m_use);
+                l *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+                m = m_new;
+                exponentiate(m_use);
+            }
+            l += rs;
+            lgkm_wait_4(vr[0][0][0], vr[0][0][1], vr[0][1][0], vr[0][1][1]);
+            lgkm_wait_4(vr[1][0][0], vr[1][0][1], vr[1][1][0], vr[1][1][1]);
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const u32x4_t pv = {pw[4 * st], pw[4 * st + 1], pw[4 * st + 2], pw[4 * st + 3]};
+                const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pv);
+#pragma unroll
+                for (int dt = 0; dt < 2; ++dt) {
+                    const u32x4_t a = {vr[st][dt][0][0], vr[st][dt][0][1], vr[st][dt][1][0], vr[st][dt][1][1]};
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), pb,
+                                                                       oacc[dt], 0, 0, 0);
+                }
+            }
+        };
+        // a block whose stage is known only at run time
+        auto body_any = [&](int j, f32x16_t& sc, f32x16_t& nxt, auto mask_tag) {
+            if constexpr (NS == 2) {
+                if (j & 1) body(j, sc, nxt, mask_tag, I1{});
+                else body(j, sc, nxt, mask_tag, I0{});
+            } else {
+                switch (j % 3) {
+                    case 0: body(j, sc, nxt, mask_tag, I0{}); break;
+                    case 1: body(j, sc, nxt, mask_tag, I1{}); break;
+                    default: body(j, sc, nxt, mask_tag, I2{}); break;
+                }
+            }
+        };
+        f32x16_t sa = qk(I0{}), sb;
+        int j = 0;
+        const int jfull = min(nfull, jhi);
+        for (; j + U - 1 < jfull; j += U) {
+            body(j, sa, sb, std::false_type{}, I0{});
+            body(j + 1, sb, sa, std::false_type{}, I1{});
+            if constexpr (U == 6) {
+                body(j + 2, sa, sb, std::false_type{}, I2{});
+                body(j + 3, sb, sa, std::false_type{}, I0{});
+                body(j + 4, sa, sb, std::false_type{}, I1{});
+                body(j + 5, sb, sa, std::false_type{}, I2{});
+            }
+        }
+        for (; j < jfull; ++j) {
+            body_any(j, sa, sb, std::false_type{});
+            sa = sb;
+        }
+        for (; j < jhi; ++j) {
+            body_any(j, sa, sb, std::true_type{});
+            sa = sb;
+        }
+    } else {
 #pragma unroll
     for (int j = 0; j < NS - 1; ++j) issue(jlo + j);
 
     int j = jlo;
     const int jfull = min(nfull, jhi);
-    // this wave's keys of a stage: rows [kh*WK, kh*WK + WK)
-    constexpr int HALF = WK * ROWB;
     for (; j < jfull; ++j) {
         wait_vmcnt<2 * LI * (NS - 2)>();      // this wave's part of block j has landed
         __syncthreads();                      // ... everyone's, and stage (j-1) % NS is free
         issue(j + NS - 1);
-        step(&ring[j % NS][0][0] + kh * HALF, j * BK + kh * WK, std::false_type{});
+        step(&ring[j % NS][0][0], j * BK, std::false_type{});
     }
     for (; j < jhi; ++j) {
         wait_vmcnt<2 * LI * (NS - 2)>();
         __syncthreads();
         issue(j + NS - 1);
-        const int kb = j * BK + kh * WK;
-        if (!CAUSAL || kb <= wq_last + off) step(&ring[j % NS][0][0] + kh * HALF, kb, std::true_type{});
+        const int kb = j * BK;
+        if (!CAUSAL || kb <= wq_last + off) step(&ring[j % NS][0][0], kb, std::true_type{});
+    }
     }
     wait_vmcnt<0>();    // no DMA may still be writing LDS when the workgroup retires
 
@@ -548,6 +694,7 @@ constexpr int kWaves = 4;
 constexpr int kStages = 3;
 constexpr int kBQ = kWaves * 32;
 constexpr int kBQHalves = kWaves / 2 * 32;   // tile rows of the key-halves variant
+constexpr int kStagesHalves = 2;             // its ring: K one block ahead of V, 32 KiB
 
 // The key-halves variant (d = 64, unsplit) takes over when the 128-row tiles
 // would leave the chip short of work: fewer than three resident tiles per
@@ -563,7 +710,7 @@ hipError_t launch_halves(const PrefillArgs& a, hipStream_t stream) {
     const int nqt = (a.Tq + kBQHalves - 1) / kBQHalves;
     const long long grid = (long long)nqt * a.B * a.H;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((prefill_bf16_kernel<64, kWaves, kStages, CAUSAL, 2>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((prefill_bf16_kernel<64, kWaves, kStagesHalves, CAUSAL, 2>), dim3((unsigned)grid),
                        dim3(kWaves * 64), 0, stream, static_cast<const uint16_t*>(a.q),
                        static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                        static_cast<uint16_t*>(a.o), a.lse, static_cast<float*>(nullptr), a.Tq, a.Tkv, a.B * a.H,
@@ -644,7 +791,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, const PrefillSplit& sp, hip
                                const char** name) {
     const int bk = block_keys(a.d);
     if (use_key_halves(a, sp.nch_max)) {
-        snprintf(g_name, sizeof g_name, "prefill_bf16_d64<waves=4,bq=%d,bk=64,key_halves=2,stages=3%s>", kBQHalves,
+        snprintf(g_name, sizeof g_name, "prefill_bf16_d64<waves=4,bq=%d,bk=64,key_halves=2,stages=%d%s>", kBQHalves, kStagesHalves,
                  a.causal ? ",causal" : "");
         *name = g_name;
         return a.causal ? launch_halves<true>(a, stream) : launch_halves<false>(a, stream);
