@@ -218,7 +218,26 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     }
     // Block j goes to stage j % NS.  Blocks past the unit's end still issue
     // (empty range, no memory traffic) so that every wave's vmcnt stays uniform.
-    auto issue = [&](int j) {
+    // (KS = 1) block j into stage S = (j - jlo) % NS; past the unit's last
+    // block the range is empty (no traffic; the base is never dereferenced)
+    auto issue = [&](int j, auto stage_tag) {
+        constexpr int S = decltype(stage_tag)::value;
+        const uint32_t kb = (uint32_t)j * BK;
+        const uint32_t bytes = j < jhi ? (uint32_t)(Tkv - (int)kb) * (uint32_t)ROWB : 0u;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)kb * D, bytes);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (size_t)kb * D, bytes);
+        uint8_t* st = &ring[S][0][0];
+#pragma unroll
+        for (int i = 0; i < LI; ++i) {
+            const int g = wave + WAVES * i;
+            buffer_load_lds_b128(rk, k_voff[i], st + g * 1024);
+            buffer_load_lds_b128(rv, v_voff[i], st + TILEB + g * 1024);
+        }
+    };
+
+    // Block j goes to stage j % NS.  Blocks past the unit's end still issue
+    // (empty range, no memory traffic) so that every wave's vmcnt stays uniform.
+    auto issue_rt = [&](int j) {
         const int kb = j * BK;
         const bool live = j < jhi;
         const uint32_t bytes = live ? (uint32_t)(Tkv - kb) * (uint32_t)ROWB : 0u;
@@ -262,7 +281,10 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     float l = 0.f;       // this lane's share of the running sum (relative to m)
 
     // One key block for this wave.  MASK applies the causal / ragged element mask.
-    auto step = [&](const uint8_t* kst, int kb, auto mask_tag) {
+    // One key block for this wave at a run-time stage (head width 128: its
+    // compile-time-stage form below needs more VGPRs than three waves per
+    // SIMD allow).  MASK applies the causal / ragged element mask.
+    auto step_rt = [&](const uint8_t* kst, int kb, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const uint8_t* vst = kst + TILEB;
         f32x16_t s[KT];
@@ -333,6 +355,103 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
                 u32x2_t hi0 = lds_read_tr16_b64<o + 8 * ROWB>(vbase + v_roff[d2]);
                 u32x2_t lo1 = lds_read_tr16_b64<o>(vbase + v_roff[d2 + 1]);
                 u32x2_t hi1 = lds_read_tr16_b64<o + 8 * ROWB>(vbase + v_roff[d2 + 1]);
+                lgkm_wait_4(lo0, hi0, lo1, hi1);
+                const u32x4_t a0 = {lo0[0], lo0[1], hi0[0], hi0[1]};
+                const u32x4_t a1 = {lo1[0], lo1[1], hi1[0], hi1[1]};
+                oacc[d2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a0), pb, oacc[d2],
+                                                                   0, 0, 0);
+                oacc[d2 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a1), pb,
+                                                                       oacc[d2 + 1], 0, 0, 0);
+            }
+        };
+        pv_step(std::integral_constant<int, 0>{});
+        pv_step(std::integral_constant<int, 1>{});
+        if constexpr (ST > 2) {
+            pv_step(std::integral_constant<int, 2>{});
+            pv_step(std::integral_constant<int, 3>{});
+        }
+    };
+
+    // (KS = 1) stage S of the ring: LDS read addresses are per-lane bases in
+    // stage 0 plus compile-time offsets
+    const uint32_t ring_lds = lds_addr(&ring[0][0][0]);
+    uint32_t k_ra1[TQ], v_ra1[DT];
+#pragma unroll
+    for (int t = 0; t < TQ; ++t) k_ra1[t] = ring_lds + k_roff[t];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) v_ra1[dt] = ring_lds + TILEB + v_roff[dt];
+    auto step = [&](auto stage_tag, int kb, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        constexpr int SO = decltype(stage_tag)::value * 2 * TILEB;
+        f32x16_t s[KT];
+        auto qk_tile = [&](auto kt_tag) {
+            constexpr int kt = decltype(kt_tag)::value;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+#pragma unroll
+            for (int t = 0; t < TQ; ++t) {
+                const bf16x8_t a = lds_load_b128<SO + kt * 32 * ROWB>(k_ra1[t]);
+                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kt], 0, 0, 0);
+            }
+        };
+        qk_tile(std::integral_constant<int, 0>{});
+        if constexpr (KT > 1) qk_tile(std::integral_constant<int, 1>{});
+        if constexpr (MASK) {
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kb + 32 * kt + 8 * (r >> 2) + 4 * hf + (r & 3);
+                    if (key > lim) s[kt][r] = kNegInf;
+                }
+        }
+        // exponentials against the current reference; packed to bf16 pairs
+        uint32_t pw[8 * KT];
+        float rs = 0.f;
+        auto exponentiate = [&](float mref) {
+            rs = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8 * KT; ++i) {
+                const int kt = i >> 3, r = 2 * (i & 7);
+                const float p0 = fast_exp2(__builtin_fmaf(s[kt][r], c, -mref));
+                const float p1 = fast_exp2(__builtin_fmaf(s[kt][r + 1], c, -mref));
+                pw[i] = pack_bf16x2(p0, p1);
+                rs += p0 + p1;
+            }
+        };
+        exponentiate(m);
+        const float row = half_swap_sum(rs);
+        if (__builtin_amdgcn_ballot_w64(!(row <= kSumLimit)) != 0) {
+            // raise the reference to the true running max and rescale
+            float mx = kNegInf;
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+            mx = half_swap_max(mx);
+            const float m_new = fmaxf(m, mx * c);
+            const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+            const float alpha = fast_exp2(m - m_use);
+            l *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+            m = m_new;
+            exponentiate(m_use);
+        }
+        l += rs;
+        auto pv_step = [&](auto st_tag) {
+            constexpr int st = decltype(st_tag)::value;
+            constexpr int o = st * 16 * ROWB;
+            const u32x4_t pv = {pw[4 * st], pw[4 * st + 1], pw[4 * st + 2], pw[4 * st + 3]};
+            const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pv);
+#pragma unroll
+            for (int d2 = 0; d2 < DT; d2 += 2) {
+                u32x2_t lo0 = lds_read_tr16_b64<SO + o>(v_ra1[d2]);
+                u32x2_t hi0 = lds_read_tr16_b64<SO + o + 8 * ROWB>(v_ra1[d2]);
+                u32x2_t lo1 = lds_read_tr16_b64<SO + o>(v_ra1[d2 + 1]);
+                u32x2_t hi1 = lds_read_tr16_b64<SO + o + 8 * ROWB>(v_ra1[d2 + 1]);
                 lgkm_wait_4(lo0, hi0, lo1, hi1);
                 const u32x4_t a0 = {lo0[0], lo0[1], hi0[0], hi0[1]};
                 const u32x4_t a1 = {lo1[0], lo1[1], hi1[0], hi1[1]};
@@ -530,24 +649,57 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
             body_any(j, sa, sb, std::true_type{});
             sa = sb;
         }
+    } else if constexpr (D == 64) {
+        // Block j sits in stage (j - jlo) % NS; the interior loop is unrolled
+        // by NS so that stages are compile-time (immediate LDS offsets).
+        static_assert(NS == 3, "the unrolled loop below assumes a 3-stage ring");
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        issue(jlo, I0{});
+        issue(jlo + 1, I1{});
+        auto blk = [&](int j, auto stage_tag, auto mask_tag) {
+            constexpr int S = decltype(stage_tag)::value;
+            wait_vmcnt<2 * LI * (NS - 2)>();  // this wave's part of block j has landed
+            __syncthreads();                  // ... everyone's, and the stage of block j-1 is free
+            issue(j + NS - 1, std::integral_constant<int, (S + NS - 1) % NS>{});
+            const int kb = j * BK;
+            if (!decltype(mask_tag)::value || !CAUSAL || kb <= wq_last + off) step(stage_tag, kb, mask_tag);
+        };
+        auto blk_any = [&](int j, auto mask_tag) {
+            switch ((j - jlo) % 3) {
+                case 0: blk(j, I0{}, mask_tag); break;
+                case 1: blk(j, I1{}, mask_tag); break;
+                default: blk(j, I2{}, mask_tag); break;
+            }
+        };
+        int j = jlo;
+        const int jfull = min(nfull, jhi);
+        for (; j + 2 < jfull; j += 3) {
+            blk(j, I0{}, std::false_type{});
+            blk(j + 1, I1{}, std::false_type{});
+            blk(j + 2, I2{}, std::false_type{});
+        }
+        for (; j < jfull; ++j) blk_any(j, std::false_type{});
+        for (; j < jhi; ++j) blk_any(j, std::true_type{});
     } else {
 #pragma unroll
-    for (int j = 0; j < NS - 1; ++j) issue(jlo + j);
+    for (int j = 0; j < NS - 1; ++j) issue_rt(jlo + j);
 
     int j = jlo;
     const int jfull = min(nfull, jhi);
     for (; j < jfull; ++j) {
         wait_vmcnt<2 * LI * (NS - 2)>();      // this wave's part of block j has landed
         __syncthreads();                      // ... everyone's, and stage (j-1) % NS is free
-        issue(j + NS - 1);
-        step(&ring[j % NS][0][0], j * BK, std::false_type{});
+        issue_rt(j + NS - 1);
+        step_rt(&ring[j % NS][0][0], j * BK, std::false_type{});
     }
     for (; j < jhi; ++j) {
         wait_vmcnt<2 * LI * (NS - 2)>();
         __syncthreads();
-        issue(j + NS - 1);
+        issue_rt(j + NS - 1);
         const int kb = j * BK;
-        if (!CAUSAL || kb <= wq_last + off) step(&ring[j % NS][0][0], kb, std::true_type{});
+        if (!CAUSAL || kb <= wq_last + off) step_rt(&ring[j % NS][0][0], kb, std::true_type{});
     }
     }
     wait_vmcnt<0>();    // no DMA may still be writing LDS when the workgroup retires
@@ -767,14 +919,19 @@ PrefillSplit prefill_bf16_split_plan(int B, int H, int Tq, int Tkv, int d, bool 
         chunk = (kv_chunk + bk - 1) / bk;
     } else {
         // automatic: split only when the query tiles alone leave the chip
-        // short of work (fewer than 3 resident tiles per compute unit), with
-        // units of an even share of all key blocks over 768 slots but never
-        // under 1024 keys -- a unit pays a few microseconds of start-up
-        // latency plus its partial's round trip, which shorter units do not
-        // earn back (measured on 1-16 heads of 1K-16K keys).
+        // short of work -- at d = 64, when even the 64-row key-halves tiles
+        // number at most one per compute unit (above that the key-halves
+        // kernel is faster than any split, measured on 1-16 heads of 1K-16K
+        // keys); at d = 128, fewer than 3 resident 128-row tiles per compute
+        // unit -- with units of an even share of all key blocks over 768
+        // slots but never under 1024 keys: a unit pays a few microseconds of
+        // start-up latency plus its partial's round trip, which shorter
+        // units do not earn back.
         const long long slots = 3LL * 256;
         const long long tiles = (long long)nqt * B * H;
-        if (tiles < slots) {
+        const bool short_of_work = d == 64 ? (long long)((Tq + kBQHalves - 1) / kBQHalves) * B * H <= 256
+                                           : tiles < slots;
+        if (short_of_work) {
             const long long share = (total * B * H + slots - 1) / slots;
             const int min_blocks = 1024 / bk;
             chunk = (int)(share < min_blocks ? min_blocks : share);

@@ -169,10 +169,15 @@ def test_split_forward_workspace_formula():
     assert attn.attn_fwd_split_workspace_bytes(4, 12, 1024, 1024, 64, True, 1024) == 0
     assert attn.attn_fwd_split_workspace_bytes(1, 1, 300, 17, 64, False, 64) == 0
     # automatic choice: many tiles -> no split; tiles of at most 1024 keys -> no split;
+    # at d = 64 more than 256 key-halves tiles (64 rows) -> no split;
     # few long tiles -> split into units of an even share (here 1 head of 16K causal
     # keys: 16512 blocks / 768 -> 22 blocks, 256-block tiles -> 12 chunks)
     assert attn.attn_fwd_split_workspace_bytes(1, 12, 16384, 16384, 64, True, 0) == 0
     assert attn.attn_fwd_split_workspace_bytes(4, 12, 1024, 1024, 64, True, 0) == 0
+    assert attn.attn_fwd_split_workspace_bytes(1, 8, 4096, 4096, 64, True, 0) == 0      # 512 tiles of 64
+    assert attn.attn_fwd_split_workspace_bytes(1, 4, 4100, 4100, 64, True, 0) == 0      # 260 tiles of 64
+    assert attn.attn_fwd_split_workspace_bytes(1, 4, 4096, 4096, 64, False, 0) > 0      # 256 tiles of 64
+    assert attn.attn_fwd_split_workspace_bytes(1, 8, 4096, 4096, 128, True, 0) > 0      # d = 128: 256 tiles of 128
     assert attn.attn_fwd_split_workspace_bytes(1, 1, 16384, 16384, 64, True, 0) == 1 * 128 * 12 * per_unit
     # 2 heads of 8K causal keys: share 11 -> 16 blocks; the 128-block tiles -> 8 chunks
     assert attn.attn_fwd_split_workspace_bytes(1, 2, 8192, 8192, 64, True, 0) == 2 * 64 * 8 * per_unit
