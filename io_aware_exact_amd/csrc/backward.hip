@@ -129,7 +129,12 @@ constexpr int KV_WAVES = 4;
 constexpr int BKV = 32 * KV_WAVES;   // keys per workgroup
 constexpr int NS = 3;                // ring stages
 
-template <int D, bool CAUSAL>
+// QS = 2 (query halves, for grids with few key tiles): the waves form
+// KV_WAVES/2 key groups of 32 keys, and the two waves of a group take the two
+// 32-row sub-tiles of every query block; the pair sums its dK, dV partials
+// through LDS at the end.  Tiles are then 64 keys and the serial query loop
+// of a tile is half as long.
+template <int D, bool CAUSAL, int QS = 1>
 __global__ __launch_bounds__(KV_WAVES * 64, BwdGeo<D>::KV_MINW)
 void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -147,20 +152,25 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     constexpr int STAGE = 2 * QBLK + 1024;
     constexpr int KV_LI = QBLK / 1024 / KV_WAVES;
     static_assert(KV_LI * KV_WAVES * 1024 == QBLK, "block rows must split evenly over the waves");
+    static_assert(QS == 1 || (QS == 2 && NSUB == 2), "query halves split a block's two sub-tiles");
+    constexpr int KG = KV_WAVES / QS;        // key groups of 32 keys
+    constexpr int BKVT = 32 * KG;            // keys per workgroup
     __shared__ __attribute__((aligned(1024))) uint8_t ring[NS][STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ln = lane & 31;
     const int hf = lane >> 5;
+    const int kg = wave % KG;                // key group
+    const int qh = wave / KG;                // query sub-tile of every block (QS = 2)
 
     // causal: the first key tiles see the most query rows, so they go first
     const int bh = blockIdx.x % BH;
     const int kt = blockIdx.x / BH;
-    const int k0 = kt * BKV;
+    const int k0 = kt * BKVT;
     const int off = Tkv - Tq;
-    const int key = k0 + 32 * wave + ln;        // this lane's key column
+    const int key = k0 + 32 * kg + ln;          // this lane's key column
 
     const size_t qbase = (size_t)bh * Tq * D;
     const size_t kvbase = (size_t)bh * Tkv * D;
@@ -187,7 +197,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     const int nqb = (Tq + BQ2 - 1) / BQ2;
     const int qb_first = CAUSAL ? max(0, k0 - off) / BQ2 : 0;
     // blocks from qb_free on are visible to every key of the tile and full
-    const int tile_last_key = min(k0 + BKV, Tkv) - 1;
+    const int tile_last_key = min(k0 + BKVT, Tkv) - 1;
     int qb_free = CAUSAL ? (max(0, tile_last_key - off) + BQ2 - 1) / BQ2 : 0;
     qb_free = max(qb_free, qb_first);
     const int qb_full_end = Tq / BQ2;             // blocks before this have no ragged rows
@@ -320,16 +330,43 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         const bool free_blk = (j >= qb_free) && (j < qb_full_end);
         // one sub-tile at a time (not unrolled: two would double the live registers)
 #pragma nounroll
-        for (int qs = 0; qs < NSUB; ++qs) {
+        for (int qs = QS == 2 ? qh : 0; qs < NSUB; qs += QS) {
             if (free_blk) {
                 subtile(st, q0, qs, std::false_type{});
-            } else if (!CAUSAL || q0 + 32 * qs + 31 + off >= k0 + 32 * wave) {
+            } else if (!CAUSAL || q0 + 32 * qs + 31 + off >= k0 + 32 * kg) {
                 // a wave whose keys all lie right of every row of a sub-tile skips it
                 subtile(st, q0, qs, std::true_type{});
             }
         }
     }
     wait_vmcnt<0>();    // no DMA may still be writing LDS when the workgroup retires
+
+    if constexpr (QS == 2) {
+        // the second wave of each key group hands its partial sums to the
+        // first through the ring (lane-major on both sides, conflict-free)
+        constexpr int NREG = 2 * DT * 16;
+        static_assert(KG * NREG * 64 * 4 <= NS * STAGE, "merge buffer must fit in the ring");
+        __syncthreads();                      // every wave is done reading the ring
+        float* xb = reinterpret_cast<float*>(&ring[0][0]) + kg * NREG * 64 + lane;
+        if (qh == 1) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    xb[(dt * 16 + r) * 64] = dkt[dt][r];
+                    xb[((DT + dt) * 16 + r) * 64] = dvt[dt][r];
+                }
+        }
+        __syncthreads();
+        if (qh == 1) return;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                dkt[dt][r] += xb[(dt * 16 + r) * 64];
+                dvt[dt][r] += xb[((DT + dt) * 16 + r) * 64];
+            }
+    }
 
     // dK = scale * (dK^T)^T, dV = (dV^T)^T: lane = key column, element r = d 32dt + 8(r/4) + 4hf + r%4
     if (key < Tkv) {
@@ -359,7 +396,12 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 constexpr int DQ_WAVES = 4;
 constexpr int BQ = 32 * DQ_WAVES;   // query rows per workgroup
 
-template <int D, bool CAUSAL>
+// KS = 2 (key halves, d = 64, for grids with few query tiles): the waves form
+// DQ_WAVES/2 row groups of 32 rows, and the two waves of a group take the two
+// 32-key halves of every key block; the pair sums its dQ partials through LDS
+// at the end.  Tiles are then 64 rows and the serial key loop of a tile is
+// half as long.
+template <int D, bool CAUSAL, int KS = 1>
 __global__ __launch_bounds__(DQ_WAVES * 64, 2)
 void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -376,26 +418,32 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     constexpr int KBLK = BK * ROWB;      // 8 KiB
     constexpr int DQ_LI = KBLK / 1024 / DQ_WAVES;
     static_assert(DQ_LI * DQ_WAVES * 1024 == KBLK, "block rows must split evenly over the waves");
+    static_assert(KS == 1 || (KS == 2 && KT == 2), "key halves split a block's two 32-key tiles");
+    constexpr int RG = DQ_WAVES / KS;        // row groups of 32 rows
+    constexpr int BQT = 32 * RG;             // query rows per workgroup
+    constexpr int WKT = KT / KS;             // 32-key tiles per wave per block
     __shared__ __attribute__((aligned(1024))) uint8_t ring[NS][2][KBLK];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ln = lane & 31;
     const int hf = lane >> 5;
+    const int rg = wave % RG;                // row group
+    const int kh = wave / RG;                // 32-key tile of every block (KS = 2)
 
     const int bh = blockIdx.x % BH;
     const int rank = blockIdx.x / BH;
     const int qt = CAUSAL ? (nqt - 1 - rank) : rank;   // heaviest tiles first
-    const int q0 = qt * BQ;
+    const int q0 = qt * BQT;
     const int off = Tkv - Tq;
     const size_t qbase = (size_t)bh * Tq * D;
     const size_t kvbase = (size_t)bh * Tkv * D;
     const uint16_t* Kh = K + kvbase;
     const uint16_t* Vh = V + kvbase;
 
-    // Q and dO fragments (B operands): row q0 + 32*wave + ln, d = 16t + 8hf + (0..7)
-    const int qrow = q0 + wave * 32 + ln;
+    // Q and dO fragments (B operands): row q0 + 32*rg + ln, d = 16t + 8hf + (0..7)
+    const int qrow = q0 + rg * 32 + ln;
     bf16x8_t qf[TQ], gf[TQ];
     float lse2 = 0.f, dd = 0.f;
     if (qrow < Tq) {
@@ -417,9 +465,9 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         }
     }
 
-    const int kend = CAUSAL ? min(Tkv, q0 + BQ + off) : Tkv;
+    const int kend = CAUSAL ? min(Tkv, q0 + BQT + off) : Tkv;
     const int nblk = (kend + BK - 1) / BK;
-    const int wq_last = q0 + wave * 32 + 31;
+    const int wq_last = q0 + rg * 32 + 31;
     const int lim = CAUSAL ? min(Tkv - 1, qrow + off) : (Tkv - 1);   // last key this row sees
 
     uint32_t voff[DQ_LI];
@@ -457,13 +505,14 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 #pragma unroll
         for (int r = 0; r < 16; ++r) dqt[dt][r] = 0.f;
 
+    // one block for this wave: its WKT 32-key tiles start at kst (kb = first key)
     auto step = [&](const uint8_t* kst, int kb, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const uint8_t* vst = kst + KBLK;
-        // S^T and dP^T for the block's keys (KT 32-key tiles); lane = query column
-        uint32_t dw[8 * KT];
+        // S^T and dP^T for the wave's keys; lane = query column
+        uint32_t dw[8 * WKT];
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
+        for (int kt = 0; kt < WKT; ++kt) {
             f32x16_t s, dp;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -505,7 +554,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         };
         kstep(std::integral_constant<int, 0>{});
         kstep(std::integral_constant<int, 1>{});
-        if constexpr (KT > 1) {
+        if constexpr (WKT > 1) {
             kstep(std::integral_constant<int, 2>{});
             kstep(std::integral_constant<int, 3>{});
         }
@@ -514,21 +563,44 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     const int nfull = CAUSAL ? min(Tkv / BK, (q0 + off + 1) / BK) : Tkv / BK;
 #pragma unroll
     for (int j = 0; j < NS - 1; ++j) issue(j);
+    // this wave's keys of a block: rows [kh * 32 * WKT, ...) of the stage
+    const int wko = KS == 2 ? kh * 32 : 0;
     int j = 0;
     for (; j < nfull; ++j) {
         wait_vmcnt<2 * DQ_LI * (NS - 2)>();
         __syncthreads();
         issue(j + NS - 1);
-        step(&ring[j % NS][0][0], j * BK, std::false_type{});
+        step(&ring[j % NS][0][0] + wko * ROWB, j * BK + wko, std::false_type{});
     }
     for (; j < nblk; ++j) {
         wait_vmcnt<2 * DQ_LI * (NS - 2)>();
         __syncthreads();
         issue(j + NS - 1);
-        const int kb = j * BK;
-        if (!CAUSAL || kb <= wq_last + off) step(&ring[j % NS][0][0], kb, std::true_type{});
+        const int kb = j * BK + wko;
+        if (!CAUSAL || kb <= wq_last + off) step(&ring[j % NS][0][0] + wko * ROWB, kb, std::true_type{});
     }
     wait_vmcnt<0>();
+
+    if constexpr (KS == 2) {
+        // the second wave of each row group hands its dQ^T partial to the
+        // first through the ring (lane-major on both sides, conflict-free)
+        constexpr int NREG = DT * 16;
+        static_assert(RG * NREG * 64 * 4 <= NS * 2 * KBLK, "merge buffer must fit in the ring");
+        __syncthreads();                      // every wave is done reading the ring
+        float* xb = reinterpret_cast<float*>(&ring[0][0][0]) + rg * NREG * 64 + lane;
+        if (kh == 1) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) xb[(dt * 16 + r) * 64] = dqt[dt][r];
+        }
+        __syncthreads();
+        if (kh == 1) return;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dqt[dt][r] += xb[(dt * 16 + r) * 64];
+    }
 
     // dQ = scale * (dQ^T)^T: lane = query row, element r = d 32dt + 8(r/4) + 4hf + r%4
     if (qrow < Tq) {
@@ -547,6 +619,16 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     }
 }
 
+// d = 64 grids with fewer than three 128-wide tiles per compute unit split
+// each tile's serial loop over a pair of waves (query halves for dK/dV, key
+// halves for dQ).
+bool bwd_kv_halves(const BackwardArgs& a) {
+    return a.d == 64 && (long long)((a.Tkv + BKV - 1) / BKV) * a.B * a.H < 3LL * 256;
+}
+bool bwd_q_halves(const BackwardArgs& a) {
+    return a.d == 64 && (long long)((a.Tq + BQ - 1) / BQ) * a.B * a.H < 3LL * 256;
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_c(const BackwardArgs& a, hipStream_t stream) {
     const int BHn = a.B * a.H;
@@ -557,17 +639,44 @@ hipError_t launch_bwd_c(const BackwardArgs& a, hipStream_t stream) {
                        static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout), a.lse, stats, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int nkt = (a.Tkv + BKV - 1) / BKV;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(nkt * BHn)), dim3(KV_WAVES * 64), 0, stream,
-                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), stats, a.dk, a.dv,
-                       a.Tq, a.Tkv, BHn, nkt, a.c, a.scale);
+    bool kv_halves = false, q_halves = false;
+    if constexpr (D == 64) {
+        kv_halves = bwd_kv_halves(a);
+        q_halves = bwd_q_halves(a);
+    }
+    if constexpr (D == 64) {
+        if (kv_halves) {
+            const int nkt = (a.Tkv + BKV / 2 - 1) / (BKV / 2);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, 2>), dim3((unsigned)(nkt * BHn)), dim3(KV_WAVES * 64), 0,
+                               stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                               static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), stats, a.dk,
+                               a.dv, a.Tq, a.Tkv, BHn, nkt, a.c, a.scale);
+        }
+    }
+    if (!kv_halves) {
+        const int nkt = (a.Tkv + BKV - 1) / BKV;
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(nkt * BHn)), dim3(KV_WAVES * 64), 0, stream,
+                           static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                           static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), stats, a.dk,
+                           a.dv, a.Tq, a.Tkv, BHn, nkt, a.c, a.scale);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int nqt = (a.Tq + BQ - 1) / BQ;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(nqt * BHn)), dim3(DQ_WAVES * 64), 0, stream,
-                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), stats, a.dq,
-                       a.Tq, a.Tkv, BHn, nqt, a.c, a.scale);
+    if constexpr (D == 64) {
+        if (q_halves) {
+            const int nqt = (a.Tq + BQ / 2 - 1) / (BQ / 2);
+            hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, 2>), dim3((unsigned)(nqt * BHn)), dim3(DQ_WAVES * 64), 0,
+                               stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                               static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), stats, a.dq,
+                               a.Tq, a.Tkv, BHn, nqt, a.c, a.scale);
+        }
+    }
+    if (!q_halves) {
+        const int nqt = (a.Tq + BQ - 1) / BQ;
+        hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(nqt * BHn)), dim3(DQ_WAVES * 64), 0, stream,
+                           static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                           static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), stats, a.dq,
+                           a.Tq, a.Tkv, BHn, nqt, a.c, a.scale);
+    }
     return hipGetLastError();
 }
 
@@ -582,8 +691,10 @@ size_t backward_workspace_bytes(int B, int H, int Tq) { return (size_t)B * H * T
 hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream, const char** name) {
     const int bq2 = a.d == 128 ? BwdGeo<128>::BQ2 : BwdGeo<64>::BQ2;
     const int bk = a.d == 128 ? BwdGeo<128>::BK : BwdGeo<64>::BK;
-    snprintf(g_name, sizeof g_name, "bwd_bf16_d%d<stats+dkdv(bk=128,bq=%d)+dq(bq=128,bk=%d)%s>", a.d, bq2, bk,
-             a.causal ? ",causal" : "");
+    const bool kvh = bwd_kv_halves(a), qh = bwd_q_halves(a);
+    snprintf(g_name, sizeof g_name, "bwd_bf16_d%d<stats+dkdv(bk=%d,bq=%d%s)+dq(bq=%d,bk=%d%s)%s>", a.d,
+             kvh ? BKV / 2 : BKV, bq2, kvh ? ",query_halves=2" : "", qh ? BQ / 2 : BQ, bk,
+             qh ? ",key_halves=2" : "", a.causal ? ",causal" : "");
     *name = g_name;
     if (a.d == 128) {
         if (a.causal) return launch_bwd_c<128, true>(a, stream);

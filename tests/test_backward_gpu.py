@@ -91,6 +91,26 @@ def test_backward_shapes(B, H, Tq, Tkv, causal, d):
     assert attn.attn_last_kernel().startswith(f"bwd_bf16_d{d}<")
 
 
+# d = 64 grids with fewer than 768 128-wide tiles split each tile's serial
+# loop over a pair of waves: query halves in dK/dV (decided by the key tiles),
+# key halves in dQ (decided by the query tiles).  Each combination:
+D64_PATH_CASES = [
+    # B, H, Tq, Tkv, causal, dK/dV query halves, dQ key halves
+    (8, 96, 129, 129, True, False, False),
+    (8, 48, 300, 100, False, True, False),
+    (8, 48, 100, 300, True, False, True),
+    (2, 5, 333, 333, True, True, True),
+]
+
+
+@pytest.mark.parametrize("B,H,Tq,Tkv,causal,kvh,qh", D64_PATH_CASES)
+def test_backward_d64_paths(B, H, Tq, Tkv, causal, kvh, qh):
+    check(Workload(f"bwd[{B},{H},{Tq},{Tkv},{'c' if causal else 'n'},d=64]", B, H, Tq, Tkv, 64, "bf16", causal,
+                   seed=300 + B * H + Tq))
+    kern = attn.attn_last_kernel()
+    assert ("query_halves=2" in kern) == kvh and ("key_halves=2" in kern) == qh, kern
+
+
 def test_backward_gpt2_full():
     check(WORKLOADS["gpt2"])
 
