@@ -11,8 +11,10 @@ online softmax, causal skipping, the epilogue).  The decode half of the path
 (split-KV kernel + combine) is timed the same way on its own workload
 (B=64, H=32, T_kv=8192, d=128, 16 partitions) and reported in "decode", and
 its grouped-query form (the same step with 8 key/value heads for the 32 query
-heads) in "decode_gqa"; "decode_b1" is one sequence (12 heads of 64, 16K
-keys) with automatically chosen partitions against one partition per head.
+heads) in "decode_gqa"; both also report the same step with the library's
+automatically chosen partition count ("automatic_splits").  "decode_b1" is
+one sequence (12 heads of 64, 16K keys) with automatically chosen partitions
+against one partition per head.
 "mid_d128" is the mid-length prefill at head width 128; "backward" is the
 backward pass (attn_bwd) on the GPT-2-shaped workload.
 "prefill_split" times one 16K-token causal head, a
@@ -188,6 +190,18 @@ def run_decode(torch, attn, steps, warmup, name="decode"):
                      device="cuda")
     total, kv = decode_bytes(w)
     unsplit = None
+    auto = None
+    if w.num_splits > 0:
+        # the same step with the library's automatic partition count, beside
+        # the workload's fixed one
+        pa = attn.attn_decode_splits(w.B, w.H, w.kv_heads, w.Tkv, w.d)
+        if pa != w.num_splits:
+            wsa = torch.empty(max(16, attn.attn_decode_workspace_bytes(w.B, w.H, w.d, pa)), dtype=torch.uint8,
+                              device="cuda")
+            msa = time_steps(torch, attn.prepared_decode(dq, dk, dv, o, lse, pa, wsa, w.scale), steps, warmup)
+            auto = {"splits": pa, "ms_per_step": msa, "value": total / (msa * 1e-3) / 1e9,
+                    "kernel": attn.attn_last_kernel()}
+            del wsa
     if w.num_splits == 0:
         # the same step in one partition per (batch, head): the shape the
         # pages measured at batch 1
@@ -235,6 +249,8 @@ def run_decode(torch, attn, steps, warmup, name="decode"):
     if unsplit is not None:
         out["unsplit"] = unsplit
         out["speedup_vs_unsplit"] = unsplit["ms_per_step"] / ms
+    if auto is not None:
+        out["automatic_splits"] = auto
     return out
 
 
