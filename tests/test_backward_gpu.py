@@ -111,6 +111,15 @@ def test_backward_d64_paths(B, H, Tq, Tkv, causal, kvh, qh):
     assert ("query_halves=2" in kern) == kvh and ("key_halves=2" in kern) == qh, kern
 
 
+def test_backward_long_head_full():
+    """One 4096-token causal head: 64 query blocks through each pair of the
+    small-grid dK/dV and dQ kernels, every gradient checked in full."""
+    w = Workload("bwd_long_head", 1, 1, 4096, 4096, 64, "bf16", True, seed=41)
+    check(w)
+    kern = attn.attn_last_kernel()
+    assert "query_halves=2" in kern and "key_halves=2" in kern, kern
+
+
 def test_backward_gpt2_full():
     check(WORKLOADS["gpt2"])
 
