@@ -448,13 +448,13 @@ def test_calls_run_on_the_current_stream():
 
 
 
-@pytest.mark.parametrize("api", ["decode", "prefill_split"])
-def test_longest_accepted_head(api):
-    """One head of 8,388,607 keys at d = 128 (K and V 2 GiB each, the largest
-    the 32-bit buffer ranges accept), sampled rows against the oracle: the
-    oracle runs on 2^20-key partitions and merges them with its own partition
-    combine."""
-    d, T = 128, (1 << 23) - 1
+@pytest.mark.parametrize("api,d", [("decode", 128), ("prefill_split", 128), ("prefill", 128), ("prefill", 64)])
+def test_longest_accepted_head(api, d):
+    """One head of the most keys the 32-bit buffer ranges accept (K and V
+    2 GiB each: 8,388,607 keys at d = 128, 16,777,215 at d = 64), sampled rows
+    against the oracle: the oracle runs on 2^20-key partitions and merges them
+    with its own partition combine."""
+    T = (1 << 31) // (2 * d) - 1
     g = torch.Generator(device="cuda").manual_seed(77)
     k = torch.randn((1, 1, T, d), generator=g, device="cuda").to(torch.bfloat16)
     v = torch.randn((1, 1, T, d), generator=g, device="cuda").to(torch.bfloat16)
@@ -465,10 +465,14 @@ def test_longest_accepted_head(api):
     if api == "decode":
         o, lse = attn.attn_decode(q, k, v, scale=scale, num_splits=0)
         lse = lse[:, :, None]
-    else:
+    elif api == "prefill_split":
         o, lse = attn.attn_fwd_split(q, k, v, causal=False, scale=scale, kv_chunk=0)
+    else:
+        o, lse = attn.attn_fwd(q, k, v, causal=False, scale=scale)
     torch.cuda.synchronize()
     say(f"  kernel {attn.attn_last_kernel()}")
+    if api == "prefill":
+        assert ("key_halves=2" in attn.attn_last_kernel()) == (d == 64)
     rows = sorted({0, tq - 1})
     qr = to_f64(q[:, :, rows])
     kh, vh = k.cpu(), v.cpu()
