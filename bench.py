@@ -123,6 +123,46 @@ def time_steps(torch, call, steps: int, warmup: int):
     return start.elapsed_time(end) / steps
 
 
+def time_cold(torch, call, reps: int = 30):
+    """Median per-call time with a 512 MiB write between calls, which evicts
+    the L2 caches and the 256 MiB last-level cache, so every call starts with
+    its inputs in HBM only (HIP events on the launch stream around each call)."""
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    call()
+    ts = []
+    for i in range(reps):
+        scrub.fill_(i & 0xFF)
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        call()
+        end.record()
+        torch.cuda.synchronize()
+        ts.append(start.elapsed_time(end))
+    del scrub
+    ts.sort()
+    return ts[len(ts) // 2], ts[0], ts[-1]
+
+
+def achievable_ceilings(torch):
+    """Measured ceilings beside the vendor peaks: a 1 GiB device copy (bytes
+    read + written per second) and a library bf16 GEMM (torch.mm, 8192^3)."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    ms_copy = time_steps(torch, lambda: dst.copy_(src), 10, 2)
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    ms_mm = time_steps(torch, lambda: torch.mm(a, b), 10, 2)
+    del a, b
+    torch.cuda.empty_cache()
+    return {"copy_GBps": 2 * (1 << 30) / (ms_copy * 1e-3) / 1e9,
+            "copy": "torch device-to-device copy of 1 GiB, read + write bytes",
+            "bf16_gemm_TFLOPs": 2 * n ** 3 / (ms_mm * 1e-3) / 1e12,
+            "gemm": "torch.mm bf16 8192 x 8192 x 8192 (library GEMM)"}
+
+
 def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -424,6 +464,9 @@ def main():
                 "frac": tflops / PEAK_BF16_TFLOPS}
     roof["traffic"] = measured_traffic("prefill", w.name)
     log(f"[bench] prefill {kern}: {ms * 1e3:.2f} us/step, {tflops:.1f} TFLOP/s")
+    cold_ms, cold_min, cold_max = time_cold(torch, call)
+    log(f"[bench] prefill with caches scrubbed between calls: {cold_ms * 1e3:.2f} us/call")
+    props = torch.cuda.get_device_properties(0)
 
     result = {
         "metric": "attn fwd TFLOP/s (causal-adjusted) & % bf16 MFMA peak (prefill); decode KV GB/s & % HBM peak",
@@ -446,7 +489,12 @@ def main():
         "pct_of_peak": {"bf16_mfma": 100.0 * tflops / PEAK_BF16_TFLOPS,
                         "hbm_algorithmic": 100.0 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS},
         "roofline": roof,
+        "cold_cache": {"ms_per_call": cold_ms, "min_ms": cold_min, "max_ms": cold_max,
+                       "value": flops / (cold_ms * 1e-3) / 1e12, "unit": "TFLOP/s",
+                       "protocol": "512 MiB write before each call, per-call HIP events, median of 30"},
         "extra_device_bytes": 0,
+        "device": {"name": torch.cuda.get_device_name(0), "arch": getattr(props, "gcnArchName", ""),
+                   "compute_units": props.multi_processor_count, "hip": torch.version.hip},
     }
     if not args.no_cpu_baseline:
         log("[bench] oracle leg on the host")
@@ -478,6 +526,12 @@ def main():
             result[name] = run_decode(torch, attn, args.steps, args.warmup, name)
             log(f"[bench] {name} {result[name]['kernel']}: {result[name]['ms_per_step']:.3f} ms/step, "
                 f"{result[name]['value']:.0f} GB/s")
+    ceil = achievable_ceilings(torch)
+    ceil["prefill_frac_of_gemm"] = tflops / ceil["bf16_gemm_TFLOPs"]
+    if "decode" in result:
+        ceil["decode_frac_of_copy"] = result["decode"]["value"] / ceil["copy_GBps"]
+    result["achievable"] = ceil
+    log(f"[bench] achievable: copy {ceil['copy_GBps']:.0f} GB/s, bf16 GEMM {ceil['bf16_gemm_TFLOPs']:.0f} TFLOP/s")
     if args.copy_calibration:
         src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
