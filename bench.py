@@ -182,11 +182,13 @@ def cpu_baseline_prefill(w, q, k, v, o_gpu, lse_gpu, min_seconds: float):
     from io_aware_exact_amd.inputs import to_f64
 
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
-    done, t_compute, err_o, err_l = 0, 0.0, 0.0, 0.0
+    done, t_compute, t_convert, err_o, err_l = 0, 0.0, 0.0, 0.0, 0.0
     t_wall0 = time.perf_counter()
     while t_compute < min_seconds:
         b, h = heads[done % len(heads)]
+        t0 = time.perf_counter()
         qb, kb, vb = to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h])
+        t_convert += time.perf_counter() - t0
         t0 = time.perf_counter()
         o_ref, lse_ref = oracle.attention(qb, kb, vb, w.scale, w.causal)
         t_compute += time.perf_counter() - t0
@@ -206,6 +208,7 @@ def cpu_baseline_prefill(w, q, k, v, o_gpu, lse_gpu, min_seconds: float):
         "sample": f"{done} (batch, head) slices of this workload ({passes:.2f} x its {len(heads)} slices), "
                   f"float64 numpy, full T_q x T_kv scores materialised per head; causal-adjusted flop count",
         "seconds": t_compute,
+        "conversion_seconds": t_convert,
         "wall_seconds": time.perf_counter() - t_wall0,
     }, {"max_abs_err_o": err_o, "max_abs_err_lse": err_l, "heads_checked": min(done, len(heads))}
 
