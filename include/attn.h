@@ -92,10 +92,13 @@ size_t attn_fwd_split_workspace_bytes(int B, int H, int Tq, int Tkv, int d, int 
  *   kv_chunk   keys per work unit, rounded up to a multiple of 64; a query tile
  *              (128 rows) whose key range is longer is split into
  *              ceil(range / kv_chunk) near-equal chunks.  0 = the library
- *              picks: it splits only when there are fewer query tiles than
- *              3 per compute unit (768), into chunks of an even share of all
- *              key blocks over 768 units but at least 1024 keys, and only
- *              tiles longer than that.
+ *              picks: it splits only when the chip is short of work -- at
+ *              d = 64 when there are at most 256 query tiles of 64 rows (one
+ *              per compute unit), at d = 128 when there are fewer than 768
+ *              tiles of 128 rows (3 per compute unit) -- into chunks of an
+ *              even share of all key blocks over 768 units but at least 1024
+ *              keys, and only tiles longer than that.  A call that does not
+ *              split runs exactly as attn_fwd.
  *   workspace  device memory of at least attn_fwd_split_workspace_bytes(...)
  *              bytes (may be NULL when that is 0); contents on entry are
  *              ignored.  Partials of split tiles: per (batch, head, tile,
