@@ -421,6 +421,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the head-width-128 prefill measurement")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache prefill calls")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle leg: seconds of CPU work")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 3 device-to-device copies of 512 MiB (a reference for HBM byte counters)")
@@ -467,8 +468,13 @@ def main():
                 "frac": tflops / PEAK_BF16_TFLOPS}
     roof["traffic"] = measured_traffic("prefill", w.name)
     log(f"[bench] prefill {kern}: {ms * 1e3:.2f} us/step, {tflops:.1f} TFLOP/s")
-    cold_ms, cold_min, cold_max = time_cold(torch, call)
-    log(f"[bench] prefill with caches scrubbed between calls: {cold_ms * 1e3:.2f} us/call")
+    cold = None
+    if not args.no_cold:
+        cold_ms, cold_min, cold_max = time_cold(torch, call)
+        log(f"[bench] prefill with caches scrubbed between calls: {cold_ms * 1e3:.2f} us/call")
+        cold = {"ms_per_call": cold_ms, "min_ms": cold_min, "max_ms": cold_max,
+                "value": flops / (cold_ms * 1e-3) / 1e12, "unit": "TFLOP/s",
+                "protocol": "512 MiB write before each call, per-call HIP events, median of 30"}
     props = torch.cuda.get_device_properties(0)
 
     result = {
@@ -492,9 +498,7 @@ def main():
         "pct_of_peak": {"bf16_mfma": 100.0 * tflops / PEAK_BF16_TFLOPS,
                         "hbm_algorithmic": 100.0 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS},
         "roofline": roof,
-        "cold_cache": {"ms_per_call": cold_ms, "min_ms": cold_min, "max_ms": cold_max,
-                       "value": flops / (cold_ms * 1e-3) / 1e12, "unit": "TFLOP/s",
-                       "protocol": "512 MiB write before each call, per-call HIP events, median of 30"},
+        "cold_cache": cold,
         "extra_device_bytes": 0,
         "device": {"name": torch.cuda.get_device_name(0), "arch": getattr(props, "gcnArchName", ""),
                    "compute_units": props.multi_processor_count, "hip": torch.version.hip},

@@ -483,11 +483,10 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
         // V, so iteration j issues K(j+NS) and V(j+NS-1), each into the stage
         // the previous iteration finished with, and every operand is still
         // requested NS-1 iterations before its use.  The interior loop is
-        // unrolled by 2*NS so that stage indices are compile-time constants
+        // unrolled by two so that stage indices are compile-time constants
         // (immediate LDS offsets) and the two score buffers alternate without
         // copies.  Units are unsplit here (jlo = 0).
-        static_assert(NS == 2 || NS == 3, "2- or 3-stage ring");
-        constexpr int U = NS == 2 ? 2 : 6;   // unroll: stages and score buffers both repeat
+        static_assert(NS == 2, "the unrolled loop below assumes a 2-stage ring");
         constexpr int HALF = WK * ROWB;
         constexpr int STAGEB = 2 * TILEB;     // bytes per ring stage (K + V)
         const uint32_t ring0 = lds_addr(&ring[0][0][0]) + (uint32_t)(kh * HALF);
@@ -526,17 +525,12 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
         };
         using I0 = std::integral_constant<int, 0>;
         using I1 = std::integral_constant<int, 1>;
-        using I2 = std::integral_constant<int, 2>;
-        issue_blk(0, I0{}, I0{});
-        issue_blk(1, I1{}, I0{});
-        issue_blk(0, I0{}, I1{});
-        if constexpr (NS == 3) {
-            issue_blk(2, I2{}, I0{});
-            issue_blk(1, I1{}, I1{});
-        }
+        issue_blk(0, I0{}, I0{});             // K(0)
+        issue_blk(1, I1{}, I0{});             // K(1)
+        issue_blk(0, I0{}, I1{});             // V(0)
         wait_vmcnt<2 * LI * (NS - 1)>();      // K(0) has landed
         __syncthreads();
-        // one block j in stage S = j % 3; sc holds S of block j, nxt receives
+        // one block j in stage S = j % 2; sc holds S of block j, nxt receives
         // S of block j+1
         auto body = [&](int j, f32x16_t& sc, f32x16_t& nxt, auto mask_tag, auto stage_tag) {
             constexpr bool MASK = decltype(mask_tag)::value;
@@ -544,8 +538,8 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
             constexpr int S1 = (S + 1) % NS, SP = (S + NS - 1) % NS;
             wait_vmcnt<2 * LI * (NS - 2)>();  // K(j+1) and V(j) have landed (this wave's part)
             __syncthreads();                  // ... everyone's; iteration j-1 is done everywhere
-            issue_blk(j + NS, stage_tag, I0{});                              // K(j+3) replaces K(j)
-            issue_blk(j + NS - 1, std::integral_constant<int, SP>{}, I1{});  // V(j+2) replaces V(j-1)
+            issue_blk(j + NS, stage_tag, I0{});                              // K(j+2) replaces K(j)
+            issue_blk(j + NS - 1, std::integral_constant<int, SP>{}, I1{});  // V(j+1) replaces V(j-1)
             if constexpr (MASK) {
                 // diagonal / ragged block (a block this wave's rows all
                 // precede is masked whole and adds nothing)
@@ -617,29 +611,15 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
         };
         // a block whose stage is known only at run time
         auto body_any = [&](int j, f32x16_t& sc, f32x16_t& nxt, auto mask_tag) {
-            if constexpr (NS == 2) {
-                if (j & 1) body(j, sc, nxt, mask_tag, I1{});
-                else body(j, sc, nxt, mask_tag, I0{});
-            } else {
-                switch (j % 3) {
-                    case 0: body(j, sc, nxt, mask_tag, I0{}); break;
-                    case 1: body(j, sc, nxt, mask_tag, I1{}); break;
-                    default: body(j, sc, nxt, mask_tag, I2{}); break;
-                }
-            }
+            if (j & 1) body(j, sc, nxt, mask_tag, I1{});
+            else body(j, sc, nxt, mask_tag, I0{});
         };
         f32x16_t sa = qk(I0{}), sb;
         int j = 0;
         const int jfull = min(nfull, jhi);
-        for (; j + U - 1 < jfull; j += U) {
+        for (; j + 1 < jfull; j += 2) {
             body(j, sa, sb, std::false_type{}, I0{});
             body(j + 1, sb, sa, std::false_type{}, I1{});
-            if constexpr (U == 6) {
-                body(j + 2, sa, sb, std::false_type{}, I2{});
-                body(j + 3, sb, sa, std::false_type{}, I0{});
-                body(j + 4, sa, sb, std::false_type{}, I1{});
-                body(j + 5, sb, sa, std::false_type{}, I2{});
-            }
         }
         for (; j < jfull; ++j) {
             body_any(j, sa, sb, std::false_type{});
