@@ -29,8 +29,10 @@
  *
  * Execution: calls are asynchronous on `stream` (NULL = the null stream) and
  * return once the kernels are enqueued; results are valid after the stream is
- * synchronised.  There is no internal synchronisation and no host<->device
- * copy.
+ * synchronised.  There is no internal synchronisation, no host<->device
+ * copy and no memset, so a call can be captured into a HIP graph (stream
+ * capture) and replayed; the kernels are deterministic, so a replay gives the
+ * same bits as a direct call.
  *
  * Errors: arguments are validated before any HIP call; a failing call
  * enqueues nothing and returns one of the negative codes below, with a
