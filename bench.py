@@ -22,9 +22,14 @@ shape with too few query tiles to fill the chip, with and without the key
 axis split across workgroups.
 
 Inputs are seeded synthetic tensors already resident in HBM when timing
-starts; W untimed warm-up steps are followed by exactly K timed steps,
+starts; W untimed warm-up steps (default 200) are followed by exactly K
+timed steps (default 2000: about 30 ms of back-to-back GPT-2-shaped calls,
+long enough for the per-call time to settle; 100-step windows read ≈ 10 %
+slower),
 bracketed by device synchronisation, with HIP events recorded on the stream
-the kernels are launched on.  The float64 oracle is timed on the host cores on
+the kernels are launched on.  "repeats" times the headline prefill and each
+decode step again as three repeats of at least 50 ms of back-to-back calls
+(per-call median and spread).  The float64 oracle is timed on the host cores on
 a bounded sample (the "cpu_baseline" leg) and checks the GPU output.
 """
 
@@ -121,6 +126,15 @@ def time_steps(torch, call, steps: int, warmup: int):
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps
+
+
+def time_repeats(torch, call, ms_per_call: float, reps: int = 3, min_ms: float = 50.0):
+    """Repeats of N back-to-back calls, N chosen so that each repeat lasts at
+    least min_ms: the per-call time of each repeat, their median and spread
+    (max - min), beside the K-step number."""
+    n = max(1, math.ceil(min_ms / max(ms_per_call, 1e-4)))
+    ts = sorted(time_steps(torch, call, n, 1) for _ in range(reps))
+    return {"calls_per_repeat": n, "ms_per_call": ts, "median_ms": ts[len(ts) // 2], "spread_ms": ts[-1] - ts[0]}
 
 
 def time_cold(torch, call, reps: int = 30):
@@ -253,6 +267,7 @@ def run_decode(torch, attn, steps, warmup, name="decode"):
     call = attn.prepared_decode(dq, dk, dv, o, lse, splits, ws, w.scale)
     ms = time_steps(torch, call, steps, warmup)
     kern = attn.attn_last_kernel()
+    reps = time_repeats(torch, call, ms)
     gbps = total / (ms * 1e-3) / 1e9
     # parity on sampled heads (oracle = the definition per head)
     rng = np.random.default_rng(5)
@@ -283,6 +298,7 @@ def run_decode(torch, attn, steps, warmup, name="decode"):
         "steps": steps,
         "warmup": warmup,
         "kernel": kern,
+        "repeats": reps,
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": gbps / PEAK_HBM_GBPS, "traffic": measured_traffic("decode", name)},
         "parity": {"max_abs_err_o": max(errs_o), "max_abs_err_lse": max(errs_l), "heads_checked": len(errs_o)},
@@ -413,8 +429,8 @@ def run_prefill_split(torch, attn, steps, warmup, name="long_1head"):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="gpt2", help="prefill workload: gpt2, mid, mid_causal, long, tiny")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurements")
     ap.add_argument("--no-split", action="store_true", help="skip the split-prefill measurement")
@@ -455,6 +471,7 @@ def main():
     call = attn.prepared_fwd(dq, dk, dv, o, lse, w.causal, w.scale, f32=(w.dtype == "f32"))
     ms = time_steps(torch, call, args.steps, args.warmup)
     kern = attn.attn_last_kernel()
+    reps = time_repeats(torch, call, ms)
     flops = prefill_flops(w)
     nbytes = prefill_bytes(w)
     tflops = flops / (ms * 1e-3) / 1e12
@@ -498,6 +515,7 @@ def main():
         "pct_of_peak": {"bf16_mfma": 100.0 * tflops / PEAK_BF16_TFLOPS,
                         "hbm_algorithmic": 100.0 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS},
         "roofline": roof,
+        "repeats": reps,
         "cold_cache": cold,
         "extra_device_bytes": 0,
         "device": {"name": torch.cuda.get_device_name(0), "arch": getattr(props, "gcnArchName", ""),

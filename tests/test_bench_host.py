@@ -1,0 +1,115 @@
+"""Host logic of bench.py (no GPU).
+
+The refusal of more than one GPU, the algorithmic flop and byte counts the
+roofline divides by (against the cost model and brute force), the digest of
+the kernel sources, and the rule that recorded HBM traffic is reported only
+while it was taken on the current sources.
+"""
+
+import importlib.util
+import json
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+from io_aware_exact_amd.inputs import WORKLOADS
+from oracle import cost
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def load_bench():
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+bench = load_bench()
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert r.stdout == ""                      # no JSON line
+    assert "one GPU" in r.stderr
+
+
+@pytest.mark.parametrize("tq,tkv", [(1, 1), (1, 7), (5, 5), (3, 9), (8, 64), (17, 40)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_visible_pairs_brute_force(tq, tkv, causal):
+    # query i sees key j when j <= i + (tkv - tq) (bottom-right causal alignment)
+    want = sum(1 for i in range(tq) for j in range(tkv) if not causal or j <= i + tkv - tq)
+    assert bench.visible_pairs(tq, tkv, causal) == want
+
+
+@pytest.mark.parametrize("name", sorted(n for n, w in WORKLOADS.items() if w.Tq > 1))
+def test_prefill_flops_match_cost_model(name):
+    w = WORKLOADS[name]
+    assert bench.prefill_flops(w) == cost.attention_flops(w.B, w.H, w.Tq, w.Tkv, w.d, w.causal)
+
+
+def test_headline_counts():
+    w = WORKLOADS["gpt2"]
+    assert bench.prefill_flops(w) == 4 * 4 * 12 * 64 * (1024 * 1025 // 2)      # 6.45 GFLOP
+    # Q, K, V, O in bf16 and the fp32 LSE, each once
+    assert bench.prefill_bytes(w) == 4 * 12 * (4 * 1024 * 64 * 2 + 1024 * 4) == 25_362_432
+    total, kv = bench.decode_bytes(WORKLOADS["decode"])
+    assert kv == 8 * 2 ** 30 == cost.kv_bytes(1, 32, 128, 8192, batch=64)
+    assert total == kv + 2 * 64 * 32 * 128 * 2 + 64 * 32 * 4
+    # grouped-query: the cache of 8 key/value heads, q / O / LSE of 32
+    total_g, kv_g = bench.decode_bytes(WORKLOADS["decode_gqa"])
+    assert kv_g == kv // 4 and total_g - kv_g == total - kv
+
+
+def copy_sources(dst):
+    src = os.path.join(ROOT, "io_aware_exact_amd", "csrc")
+    os.makedirs(os.path.join(dst, "io_aware_exact_amd"))
+    shutil.copytree(src, os.path.join(dst, "io_aware_exact_amd", "csrc"))
+    return os.path.join(dst, "io_aware_exact_amd", "csrc")
+
+
+def test_digest_ignores_comments_not_code(tmp_path, monkeypatch):
+    csrc = copy_sources(str(tmp_path))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    base = bench.kernel_sources_digest()
+    assert base == load_bench().kernel_sources_digest()   # same text, same digest
+    path = os.path.join(csrc, "decode.hip")
+    with open(path) as f:
+        text = f.read()
+    with open(path, "w") as f:
+        f.write("// a new comment\n/* and a block\n   comment */\n" + text.replace("\n", "\n\n", 3))
+    assert bench.kernel_sources_digest() == base
+    with open(path, "w") as f:
+        f.write(text + "\nstatic int extra_symbol = 1;\n")
+    assert bench.kernel_sources_digest() != base
+
+
+def test_traffic_reported_only_for_current_sources(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    assert bench.measured_traffic("prefill", "gpt2") is None          # no record
+    rec = {"gpt2": {"prefill": {"sources_sha256_16": bench.kernel_sources_digest(),
+                                "fetch_bytes": 1000.4, "write_bytes": 24.0}}}
+    with open(os.path.join(tmp_path, "traffic.json"), "w") as f:
+        json.dump(rec, f)
+    assert bench.measured_traffic("prefill", "gpt2") == 1024
+    assert bench.measured_traffic("decode", "gpt2") is None
+    rec["gpt2"]["prefill"]["sources_sha256_16"] = "0" * 16
+    with open(os.path.join(tmp_path, "traffic.json"), "w") as f:
+        json.dump(rec, f)
+    assert bench.measured_traffic("prefill", "gpt2") is None          # taken on other sources
+
+
+def test_committed_counters_were_taken_on_these_sources():
+    with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+        rec = json.load(f)
+    digest = bench.kernel_sources_digest()
+    entries = [(wl, k, e) for wl, by in rec.items() if isinstance(by, dict)
+               for k, e in by.items() if isinstance(e, dict) and "sources_sha256_16" in e]
+    assert entries
+    stale = [(wl, k) for wl, k, e in entries if e["sources_sha256_16"] != digest]
+    assert not stale, f"HBM counters recorded on other kernel sources: {stale}"
