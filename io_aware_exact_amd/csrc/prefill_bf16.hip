@@ -216,10 +216,10 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
         k_voff[i] = (uint32_t)(row * ROWB + ((slot ^ G::swz_k(row)) << 4));
         v_voff[i] = (uint32_t)(row * ROWB + ((slot ^ G::swz_v(row)) << 4));
     }
-    // Block j goes to stage j % NS.  Blocks past the unit's end still issue
-    // (empty range, no memory traffic) so that every wave's vmcnt stays uniform.
-    // (KS = 1) block j into stage S = (j - jlo) % NS; past the unit's last
-    // block the range is empty (no traffic; the base is never dereferenced)
+    // (128-row tiles, head width 64) DMA of K and V block j into stage
+    // S = (j - jlo) % NS.  Blocks past the unit's end still issue, with an
+    // empty range (no memory traffic; the base is never dereferenced), so that
+    // every wave's vmcnt count stays uniform.
     auto issue = [&](int j, auto stage_tag) {
         constexpr int S = decltype(stage_tag)::value;
         const uint32_t kb = (uint32_t)j * BK;
@@ -235,8 +235,8 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
         }
     };
 
-    // Block j goes to stage j % NS.  Blocks past the unit's end still issue
-    // (empty range, no memory traffic) so that every wave's vmcnt stays uniform.
+    // (head width 128) the same with the stage chosen at run time: block j
+    // goes to stage j % NS.
     auto issue_rt = [&](int j) {
         const int kb = j * BK;
         const bool live = j < jhi;
@@ -280,7 +280,6 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     float m = kNegInf;   // reference max of S * c (log2 units), raised only when needed
     float l = 0.f;       // this lane's share of the running sum (relative to m)
 
-    // One key block for this wave.  MASK applies the causal / ragged element mask.
     // One key block for this wave at a run-time stage (head width 128: its
     // compile-time-stage form below needs more VGPRs than three waves per
     // SIMD allow).  MASK applies the causal / ragged element mask.

@@ -10,10 +10,11 @@ float64 (it does not use the GPU's O or LSE).
 
 Tolerance: max-abs error <= 2e-2 * max(1, max|reference|) per gradient.
 Derivation: P and dS enter the MFMA products rounded to bf16 (relative error
-at most 2^-9 per term); the forward's O, used for the row constant D, carries
+at most 2^-8 per term, the unit roundoff of an 8-bit significand); the
+forward's O, used for the row constant D, carries
 the same rounding; summed over up to T_q rows with independent signs the
-relative error of a gradient entry stays a small multiple of 2^-9 = 2e-3, and
-the bound keeps a 10x margin over that, the same margin as the forward's 2e-2
+relative error of a gradient entry stays a small multiple of 2^-8 = 3.9e-3, and
+the bound keeps a 5x margin over that, the same margin as the forward's 2e-2
 bf16 bar on O.
 """
 
