@@ -171,10 +171,44 @@ def achievable_ceilings(torch):
     ms_mm = time_steps(torch, lambda: torch.mm(a, b), 10, 2)
     del a, b
     torch.cuda.empty_cache()
-    return {"copy_GBps": 2 * (1 << 30) / (ms_copy * 1e-3) / 1e9,
-            "copy": "torch device-to-device copy of 1 GiB, read + write bytes",
-            "bf16_gemm_TFLOPs": 2 * n ** 3 / (ms_mm * 1e-3) / 1e12,
-            "gemm": "torch.mm bf16 8192 x 8192 x 8192 (library GEMM)"}
+    out = {"copy_GBps": 2 * (1 << 30) / (ms_copy * 1e-3) / 1e9,
+           "copy": "torch device-to-device copy of 1 GiB, read + write bytes",
+           "bf16_gemm_TFLOPs": 2 * n ** 3 / (ms_mm * 1e-3) / 1e12,
+           "gemm": "torch.mm bf16 8192 x 8192 x 8192 (library GEMM)"}
+    rate = mfma_loop_rate(torch)
+    if rate is not None:
+        out["mfma_loop_TFLOPs"] = rate
+        out["mfma_loop"] = ("matrix-pipe probe (libattn_probe.so): 2048 workgroups of 4 waves, each wave 4 "
+                            "independent chains of v_mfma_f32_32x32x16_bf16 from registers, 4096 steps")
+    return out
+
+
+def mfma_loop_rate(torch, blocks: int = 2048, iters: int = 4096):
+    """bf16 MFMA rate the chip sustains under load (TFLOP/s): the probe kernel
+    of libattn_probe.so, timed with HIP events on the current stream; None if
+    the probe library is not built."""
+    import ctypes
+
+    path = os.path.join(ROOT, "io_aware_exact_amd", "libattn_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.probe_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.probe_mfma_loop.restype = ctypes.c_int
+    lib.probe_mfma_loop_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.probe_mfma_loop_flops.restype = ctypes.c_double
+    lib.probe_mfma_loop_threads.restype = ctypes.c_int
+    out = torch.empty(blocks * lib.probe_mfma_loop_threads(), dtype=torch.float32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def call():
+        rc = lib.probe_mfma_loop(blocks, iters, ctypes.c_void_p(out.data_ptr()), stream)
+        if rc != 0:
+            raise RuntimeError(f"MFMA probe launch failed (hipError {rc})")
+
+    ms = time_steps(torch, call, 10, 3)
+    del out
+    return lib.probe_mfma_loop_flops(blocks, iters) / (ms * 1e-3) / 1e12
 
 
 def blas_threads() -> int:
@@ -553,10 +587,15 @@ def main():
                 f"{result[name]['value']:.0f} GB/s")
     ceil = achievable_ceilings(torch)
     ceil["prefill_frac_of_gemm"] = tflops / ceil["bf16_gemm_TFLOPs"]
+    if "mfma_loop_TFLOPs" in ceil:
+        ceil["prefill_frac_of_mfma_loop"] = tflops / ceil["mfma_loop_TFLOPs"]
+        if "mid_d128" in result:
+            ceil["mid_d128_frac_of_mfma_loop"] = result["mid_d128"]["value"] / ceil["mfma_loop_TFLOPs"]
     if "decode" in result:
         ceil["decode_frac_of_copy"] = result["decode"]["value"] / ceil["copy_GBps"]
     result["achievable"] = ceil
-    log(f"[bench] achievable: copy {ceil['copy_GBps']:.0f} GB/s, bf16 GEMM {ceil['bf16_gemm_TFLOPs']:.0f} TFLOP/s")
+    log(f"[bench] achievable: copy {ceil['copy_GBps']:.0f} GB/s, bf16 GEMM {ceil['bf16_gemm_TFLOPs']:.0f} TFLOP/s, "
+        f"MFMA loop {ceil.get('mfma_loop_TFLOPs', float('nan')):.0f} TFLOP/s")
     if args.copy_calibration:
         src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)

@@ -2,6 +2,10 @@
 
     python -m io_aware_exact_amd.build          # compile every source for gfx950 and link
 
+Also builds io_aware_exact_amd/libattn_probe.so from probe/: a matrix-pipe
+throughput probe the benchmark times beside the attention kernels (not part of
+the attention library or its C ABI).
+
 Every .hip source is compiled for gfx950 only; the C ABI (api.cpp) is host
 C++.  Packed fp32 VALU instructions are disabled in device code.
 """
@@ -20,6 +24,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn.so")
+PROBE = os.path.join(PKG, "probe")
+PROBE_LIB = os.path.join(PKG, "libattn_probe.so")
 
 ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -37,9 +43,9 @@ def sources():
     return sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str) -> str:
+def _compile(src: str, where: str = CSRC) -> str:
     obj = os.path.join(BUILD, src + ".o")
-    path = os.path.join(CSRC, src)
+    path = os.path.join(where, src)
     if src.endswith(".hip"):
         cmd = [hipcc(), *COMMON, f"--offload-arch={ARCH}", *DEVICE_FLAGS, "-c", path, "-o", obj]
     else:
@@ -67,7 +73,23 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB} from {', '.join(srcs)}")
+    build_probe(verbose)
     return LIB
+
+
+def build_probe(verbose: bool = False) -> str:
+    """Compile probe/*.hip and link libattn_probe.so."""
+    srcs = sorted(f for f in os.listdir(PROBE) if f.endswith(".hip"))
+    objs = [_compile(f, PROBE) for f in srcs]
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print(f"built {PROBE_LIB} from {', '.join(srcs)}")
+    return PROBE_LIB
 
 
 if __name__ == "__main__":

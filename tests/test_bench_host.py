@@ -113,3 +113,21 @@ def test_committed_counters_were_taken_on_these_sources():
     assert entries
     stale = [(wl, k) for wl, k, e in entries if e["sources_sha256_16"] != digest]
     assert not stale, f"HBM counters recorded on other kernel sources: {stale}"
+
+
+def test_mfma_probe_library_exports():
+    import ctypes
+
+    path = os.path.join(ROOT, "io_aware_exact_amd", "libattn_probe.so")
+    if not os.path.exists(path):
+        pytest.skip("probe library not built")
+    lib = ctypes.CDLL(path)
+    lib.probe_mfma_loop_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.probe_mfma_loop_flops.restype = ctypes.c_double
+    lib.probe_mfma_loop_threads.restype = ctypes.c_int
+    lib.probe_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.probe_mfma_loop_threads() == 256
+    # blocks x 4 waves x iters x 4 MFMAs x (32*32*16*2) flops
+    assert lib.probe_mfma_loop_flops(2048, 4096) == 2048 * 4 * 4096 * 4 * 32768
+    assert lib.probe_mfma_loop(0, 1, None, None) != 0            # rejected before any launch
+    assert lib.probe_mfma_loop(1, 1, None, None) != 0
