@@ -22,10 +22,10 @@ shape with too few query tiles to fill the chip, with and without the key
 axis split across workgroups.
 
 Inputs are seeded synthetic tensors already resident in HBM when timing
-starts; W untimed warm-up steps (default 200) are followed by exactly K
-timed steps (default 2000: about 30 ms of back-to-back GPT-2-shaped calls,
-long enough for the per-call time to settle; 100-step windows read ≈ 10 %
-slower),
+starts; W untimed warm-up steps (default 1000, ≈ 15 ms of GPT-2-shaped
+calls: the first ≈ 8 ms of back-to-back calls after an idle host phase run
+slower while the clock settles) are followed by exactly K timed steps
+(default 2000, ≈ 30 ms),
 bracketed by device synchronisation, with HIP events recorded on the stream
 the kernels are launched on.  "repeats" times the headline prefill and each
 decode step again as three repeats of at least 50 ms of back-to-back calls
@@ -464,7 +464,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default="gpt2", help="prefill workload: gpt2, mid, mid_causal, long, tiny")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurements")
     ap.add_argument("--no-split", action="store_true", help="skip the split-prefill measurement")
