@@ -70,6 +70,9 @@ enum {
  * the output accumulator are fp32 ("IO-Aware Attention", section "Where the
  * approach stops helping": 32-bit accumulation and rescaling); P is rounded to
  * bf16 (nearest even) before the PV product and O is rounded once at the end.
+ * Those two roundings, each at most 2^-8 relative, bound every element:
+ * |O - O_exact| <= 2^-8 (|O_exact| + A) plus fp32 rounding, where A is the
+ * attention output with |V| as values (so at most 2^-7 max|V| for a row).
  * Supported: d in {64, 128} (64- and 32-key blocks); for T_q == 1 the decode
  * kernel runs unsplit (no workspace).  T_q and T_kv need not be multiples of
  * any tile.
@@ -228,7 +231,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
 /*
  * attn_last_kernel -- name and tile configuration of the kernel(s) enqueued by
  * this thread's last successful call, e.g.
- * "prefill_bf16_d64<waves=4,bq=128,bk=64,causal>" ("Attention and Its
+ * "prefill_bf16_d64<waves=4,bq=128,bk=64,stages=3,causal>" ("Attention and Its
  * Computational Cost", section "Which kernel ran": a measurement of attention
  * names the kernel that ran).  Empty before the first call.  The string is
  * thread-local and valid until this thread's next call.
