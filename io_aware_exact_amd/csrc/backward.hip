@@ -139,7 +139,7 @@ __global__ __launch_bounds__(KV_WAVES * 64, BwdGeo<D>::KV_MINW)
 void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                      const float2* __restrict__ stats, float* __restrict__ dK, float* __restrict__ dV,
-                     int Tq, int Tkv, int BH, int nkt, float c, float scale) {
+                     int Tq, int Tkv, int BH, float c, float scale) {
     using G = BwdGeo<D>;
     constexpr int ROWB = D * 2;
     constexpr int TQ = D / 16;
@@ -650,7 +650,7 @@ hipError_t launch_bwd_c(const BackwardArgs& a, hipStream_t stream) {
             hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, 2>), dim3((unsigned)(nkt * BHn)), dim3(KV_WAVES * 64), 0,
                                stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                                static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), stats, a.dk,
-                               a.dv, a.Tq, a.Tkv, BHn, nkt, a.c, a.scale);
+                               a.dv, a.Tq, a.Tkv, BHn, a.c, a.scale);
         }
     }
     if (!kv_halves) {
@@ -658,7 +658,7 @@ hipError_t launch_bwd_c(const BackwardArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(nkt * BHn)), dim3(KV_WAVES * 64), 0, stream,
                            static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                            static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), stats, a.dk,
-                           a.dv, a.Tq, a.Tkv, BHn, nkt, a.c, a.scale);
+                           a.dv, a.Tq, a.Tkv, BHn, a.c, a.scale);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if constexpr (D == 64) {

@@ -22,7 +22,7 @@ template <int D>
 __global__ __launch_bounds__(64)
 void prefill_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                         const float* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE,
-                        int Tq, int Tkv, int BH, int nqt, int causal, float c) {
+                        int Tq, int Tkv, int BH, int causal, float c) {
     constexpr int TPQ = (D > 64) ? 2 : 1;
     constexpr int DPT = D / TPQ;
     constexpr int QPW = 64 / TPQ;
@@ -110,7 +110,7 @@ hipError_t launch_d(const PrefillArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((prefill_f32_kernel<D>), dim3((unsigned)grid), dim3(64), 0, stream,
                        static_cast<const float*>(a.q), static_cast<const float*>(a.k),
                        static_cast<const float*>(a.v), static_cast<float*>(a.o), a.lse, a.Tq, a.Tkv,
-                       a.B * a.H, nqt, a.causal ? 1 : 0, a.c);
+                       a.B * a.H, a.causal ? 1 : 0, a.c);
     return hipGetLastError();
 }
 
