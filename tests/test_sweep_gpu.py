@@ -12,7 +12,13 @@ nearly uniform rows to rows whose softmax is a single key; the latter drive
 the kernels' reference-max raises far more often than N(0,1) inputs do.
 
 Tolerances.  LSE max-abs <= 1e-3 and gradients <= 2e-2 * max(1,
-max|reference|), as in the other parity files; fp32 O max-abs <= 1e-5.  For
+max|reference|), as in the other parity files.  fp32 O: max-abs <= the larger
+of 1e-5 and twice the error that a plain float32 evaluation of the definition
+(numpy, here in the test) makes on the same inputs.  At these scales logits
+reach magnitude 100 and more, and their fp32 rounding alone moves O by
+1e-5-5e-5 (numpy float32 evaluations err by 1.8e-5 to 4.5e-5 on such a case,
+depending on the summation order), while the
+1e-5 bar of the fp32 workload holds at its default scale.  For
 bf16 O the 2e-2 max-abs bar of the benchmark workloads (N(0,1) inputs at the
 default scale, where rows spread their weight) does not carry over to rows
 whose softmax is nearly one-hot: there O is close to a single row of V, with
@@ -82,8 +88,9 @@ def qkv(seed, B, H, Hkv, Tq, Tkv, d, dtype, kf):
     return q, k, v
 
 
-def compare(o, lse, o_ref, lse_ref, dtype, a_ref=None):
-    """a_ref: the oracle's attention output with |V| as values (bf16 only)."""
+def compare(o, lse, o_ref, lse_ref, dtype, a_ref=None, tol_f32=None):
+    """a_ref: the oracle's attention output with |V| as values (bf16 only);
+    tol_f32: the fp32 max-abs bar (default TOL_O["f32"])."""
     g = to_f64(o)
     assert np.isfinite(g).all()
     err = np.abs(g - o_ref)
@@ -94,8 +101,9 @@ def compare(o, lse, o_ref, lse_ref, dtype, a_ref=None):
         say(f"  max|dO|={err.max():.3e}, max err/bound={ratio:.3f}, max|dLSE|={el:.3e}")
         assert ratio <= 1.0, f"O error {err.max()} exceeds the two-rounding bound (ratio {ratio})"
     else:
-        say(f"  max|dO|={err.max():.3e} (tol {TOL_O[dtype]}), max|dLSE|={el:.3e}")
-        assert float(err.max()) <= TOL_O[dtype], f"O error {err.max()}"
+        tol = TOL_O[dtype] if tol_f32 is None else tol_f32
+        say(f"  max|dO|={err.max():.3e} (tol {tol:.3e}), max|dLSE|={el:.3e}")
+        assert float(err.max()) <= tol, f"O error {err.max()}"
     assert el <= TOL_LSE, f"LSE error {el}"
 
 
@@ -182,7 +190,21 @@ def test_sweep_fp32(i, B, H, Tq, Tkv, d, causal, scale, kf):
     torch.cuda.synchronize()
     say(f"  kernel {attn.attn_last_kernel()}")
     o_ref, lse_ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), scale, causal)
-    compare(o, lse, o_ref, lse_ref, "f32")
+    tol = max(TOL_O["f32"], 2.0 * float32_definition_error(q, k, v, scale, causal, o_ref))
+    compare(o, lse, o_ref, lse_ref, "f32", tol_f32=tol)
+
+
+def float32_definition_error(q, k, v, scale, causal, o_ref):
+    """Max-abs error, against the float64 oracle, of the definition evaluated
+    in float32 arithmetic (numpy): the accuracy fp32 itself allows here."""
+    q32, k32, v32 = (t.numpy().astype(np.float32) for t in (q, k, v))
+    s = np.matmul(q32, np.swapaxes(k32, -1, -2)) * np.float32(scale)
+    if causal:
+        tq, tkv = s.shape[-2], s.shape[-1]
+        s = np.where(np.arange(tkv)[None, :] > np.arange(tq)[:, None] + (tkv - tq), np.float32(-np.inf), s)
+    p = np.exp(s - s.max(axis=-1, keepdims=True))
+    o32 = np.matmul(p, v32) / p.sum(axis=-1, keepdims=True)
+    return float(np.abs(o32.astype(np.float64) - o_ref).max())
 
 
 def backward_cases(n, seed):
