@@ -480,7 +480,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the attention forward has no multi-GPU path in this build.", file=sys.stderr)
+              "the library has no multi-GPU path (each GPU would run its own shard; see the sharding design).", file=sys.stderr)
         sys.exit(2)
 
     import torch
