@@ -71,6 +71,15 @@ __device__ __forceinline__ bf16x8_t lds_load_b128(uint32_t addr) {
     return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>((uintptr_t)(addr + OFF));
 }
 
+// LDS DMA of 16 bytes per lane with a constant added (in the instruction's
+// offset field, so inside the buffer range check) to both the global and the
+// LDS address.
+template <int OFF>
+__device__ __forceinline__ void buffer_load_lds_b128_off(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds_base) {
+    static_assert(OFF >= 0 && OFF < 4096, "12-bit instruction offset");
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 16, (int)voff, 0, OFF, 0);
+}
+
 // Tile geometry per head width.  Rows are D*2 bytes; LDS chunk swizzles
 // (16-byte chunk index within a row) make the K operand reads (ds_read_b128,
 // 32 rows x one chunk pair per instruction) and the V transposed reads (8
@@ -497,18 +506,25 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
         // DMA of block b into stage S: the descriptor covers block b to the
         // end of the head (empty past the end: no memory traffic, and its
         // base is then never dereferenced)
+        // DMA: wave w moves the 1 KiB row groups g0 and g0 + 2 (16 rows apart,
+        // so both rows have the same chunk swizzle and the second load is the
+        // first plus 2 KiB on both the global and the LDS side: one offset
+        // register per operand, the 2 KiB in the instruction's offset field)
+        static_assert(LI == 2 && RPG == 8 && WAVES == 4, "row-group mapping of the key-halves DMA");
+        const int g0 = (wave & 1) + 4 * (wave >> 1);
+        const int row0 = RPG * g0 + lane / CPR;
+        const int slot0 = lane % CPR;
+        const uint32_t k_voff0 = (uint32_t)(row0 * ROWB + ((slot0 ^ G::swz_k(row0)) << 4));
+        const uint32_t v_voff0 = (uint32_t)(row0 * ROWB + ((slot0 ^ G::swz_v(row0)) << 4));
         auto issue_blk = [&](int b, auto stage_tag, auto which_tag) {
             constexpr int S = decltype(stage_tag)::value;
             constexpr int W = decltype(which_tag)::value;
             const uint32_t kb = (uint32_t)b * BK;
             const uint32_t bytes = (uint32_t)max(Tkv - (int)kb, 0) * (uint32_t)ROWB;
             const __amdgpu_buffer_rsrc_t rs = make_rsrc((W ? Vh : Kh) + (size_t)kb * D, bytes);
-            uint8_t* st = &ring[S][W][0];
-#pragma unroll
-            for (int i = 0; i < LI; ++i) {
-                const int g = wave + WAVES * i;
-                buffer_load_lds_b128(rs, W ? v_voff[i] : k_voff[i], st + g * 1024);
-            }
+            uint8_t* st = &ring[S][W][0] + g0 * 1024;
+            buffer_load_lds_b128_off<0>(rs, W ? v_voff0 : k_voff0, st);
+            buffer_load_lds_b128_off<2048>(rs, W ? v_voff0 : k_voff0, st);
         };
         auto qk = [&](auto stage_tag) {
             constexpr int S = decltype(stage_tag)::value;
@@ -616,6 +632,15 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
         f32x16_t sa = qk(I0{}), sb;
         int j = 0;
         const int jfull = min(nfull, jhi);
+        if (jfull > 0) {
+            // block 0 is unmasked for every row: start the reference at this
+            // wave's row max over it, so the first block takes the plain path
+            // instead of the rescale pass (a masked block 0 keeps m = -inf)
+            float mx = kNegInf;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sa[r]);
+            m = half_swap_max(mx) * c;
+        }
         for (; j + 1 < jfull; j += 2) {
             body(j, sa, sb, std::false_type{}, I0{});
             body(j + 1, sb, sa, std::false_type{}, I1{});
