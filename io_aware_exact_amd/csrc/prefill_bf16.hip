@@ -215,7 +215,8 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     const int wq_last = wq_first + 31;
     const int lim = CAUSAL ? min(Tkv - 1, qrow + off) : (Tkv - 1);   // last key this row may see
 
-    // ---- DMA loads: wave w moves row groups g = w + WAVES*i (RPG rows = 1 KiB each) ----
+    // ---- DMA loads (head width 128): wave w moves row groups g = w + WAVES*i
+    // (RPG rows = 1 KiB each) ----
     uint32_t k_voff[LI], v_voff[LI];
 #pragma unroll
     for (int i = 0; i < LI; ++i) {
@@ -225,23 +226,33 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
         k_voff[i] = (uint32_t)(row * ROWB + ((slot ^ G::swz_k(row)) << 4));
         v_voff[i] = (uint32_t)(row * ROWB + ((slot ^ G::swz_v(row)) << 4));
     }
+    // ---- DMA loads (head width 64): wave w moves the 1 KiB row groups g0 and
+    // g0 + 2, with g0 = (w mod 2) + 4 (w / 2).  The two are 16 rows apart, where
+    // the K and V chunk swizzles (functions of row bits 1-3) agree, so the
+    // second load is the first plus 2 KiB in the instruction's offset field
+    // (applied to the global and the LDS address alike, inside the buffer
+    // range check): one offset register per operand.  At head width 128 the
+    // matching rows are 4 KiB apart, past the 12-bit offset field. ----
+    const int g0 = (wave & 1) + 4 * (wave >> 1);
+    const int row0 = RPG * g0 + lane / CPR;
+    const uint32_t k_voff0 = (uint32_t)(row0 * ROWB + (((lane % CPR) ^ G::swz_k(row0)) << 4));
+    const uint32_t v_voff0 = (uint32_t)(row0 * ROWB + (((lane % CPR) ^ G::swz_v(row0)) << 4));
     // (128-row tiles, head width 64) DMA of K and V block j into stage
     // S = (j - jlo) % NS.  Blocks past the unit's end still issue, with an
     // empty range (no memory traffic; the base is never dereferenced), so that
     // every wave's vmcnt count stays uniform.
     auto issue = [&](int j, auto stage_tag) {
+        static_assert(D == 64 && LI == 2 && RPG == 8 && WAVES == 4, "row-group mapping of the head-width-64 DMA");
         constexpr int S = decltype(stage_tag)::value;
         const uint32_t kb = (uint32_t)j * BK;
         const uint32_t bytes = j < jhi ? (uint32_t)(Tkv - (int)kb) * (uint32_t)ROWB : 0u;
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)kb * D, bytes);
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (size_t)kb * D, bytes);
-        uint8_t* st = &ring[S][0][0];
-#pragma unroll
-        for (int i = 0; i < LI; ++i) {
-            const int g = wave + WAVES * i;
-            buffer_load_lds_b128(rk, k_voff[i], st + g * 1024);
-            buffer_load_lds_b128(rv, v_voff[i], st + TILEB + g * 1024);
-        }
+        uint8_t* st = &ring[S][0][0] + g0 * 1024;
+        buffer_load_lds_b128_off<0>(rk, k_voff0, st);
+        buffer_load_lds_b128_off<2048>(rk, k_voff0, st);
+        buffer_load_lds_b128_off<0>(rv, v_voff0, st + TILEB);
+        buffer_load_lds_b128_off<2048>(rv, v_voff0, st + TILEB);
     };
 
     // (head width 128) the same with the stage chosen at run time: block j
@@ -506,16 +517,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
         // DMA of block b into stage S: the descriptor covers block b to the
         // end of the head (empty past the end: no memory traffic, and its
         // base is then never dereferenced)
-        // DMA: wave w moves the 1 KiB row groups g0 and g0 + 2 (16 rows apart,
-        // so both rows have the same chunk swizzle and the second load is the
-        // first plus 2 KiB on both the global and the LDS side: one offset
-        // register per operand, the 2 KiB in the instruction's offset field)
-        static_assert(LI == 2 && RPG == 8 && WAVES == 4, "row-group mapping of the key-halves DMA");
-        const int g0 = (wave & 1) + 4 * (wave >> 1);
-        const int row0 = RPG * g0 + lane / CPR;
-        const int slot0 = lane % CPR;
-        const uint32_t k_voff0 = (uint32_t)(row0 * ROWB + ((slot0 ^ G::swz_k(row0)) << 4));
-        const uint32_t v_voff0 = (uint32_t)(row0 * ROWB + ((slot0 ^ G::swz_v(row0)) << 4));
+        static_assert(LI == 2 && RPG == 8 && WAVES == 4, "row-group mapping of the head-width-64 DMA");
         auto issue_blk = [&](int b, auto stage_tag, auto which_tag) {
             constexpr int S = decltype(stage_tag)::value;
             constexpr int W = decltype(which_tag)::value;
