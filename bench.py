@@ -50,6 +50,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+PEAK_F32_VALU_TFLOPS = 157.3  # MI355X fp32 vector (256 CUs x 4 SIMDs x 16 lanes x 2 (FMA) x 2 (packed) x 2.4 GHz)
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -509,14 +510,17 @@ def main():
     flops = prefill_flops(w)
     nbytes = prefill_bytes(w)
     tflops = flops / (ms * 1e-3) / 1e12
-    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    # bf16 products run on the matrix cores; the fp32 path's are VALU FMAs
+    compute_peak, compute_bound = ((PEAK_BF16_TFLOPS, "mfma") if w.dtype == "bf16"
+                                   else (PEAK_F32_VALU_TFLOPS, "alu"))
+    t_mfma = flops / (compute_peak * 1e12)
     t_hbm = nbytes / (PEAK_HBM_GBPS * 1e9)
     if t_hbm > t_mfma:
         ach = nbytes / (ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBPS}
     else:
-        roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": tflops / PEAK_BF16_TFLOPS}
+        roof = {"bound": compute_bound, "achieved": tflops, "peak": compute_peak, "unit": "TFLOP/s",
+                "frac": tflops / compute_peak}
     roof["traffic"] = measured_traffic("prefill", w.name)
     log(f"[bench] prefill {kern}: {ms * 1e3:.2f} us/step, {tflops:.1f} TFLOP/s")
     cold = None
@@ -546,7 +550,7 @@ def main():
                    "B": w.B, "H": w.H, "Tq": w.Tq, "Tkv": w.Tkv, "d": w.d, "causal": w.causal,
                    "scale": w.scale, "parallelism": "none (1 GPU)"},
         "kernel": kern,
-        "pct_of_peak": {"bf16_mfma": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "pct_of_peak": {("bf16_mfma" if w.dtype == "bf16" else "f32_valu"): 100.0 * tflops / compute_peak,
                         "hbm_algorithmic": 100.0 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS},
         "roofline": roof,
         "repeats": reps,
