@@ -201,7 +201,8 @@ def combine_partials(o_parts, lse_parts):
         lse = M + ln(sum_p w_p),  O = sum_p w_p O_p / sum_p w_p.
 
     o_parts: (P, ..., d_v), lse_parts: (P, ...).  Partitions with lse = -inf
-    (no keys) get zero weight.
+    (no keys) get zero weight; their outputs must be finite (0 * nan is nan).
+    At least one partition of each row must have keys.
     """
     o_parts = _as_f64(o_parts)
     lse_parts = _as_f64(lse_parts)

@@ -440,6 +440,36 @@ def test_split_combine_equals_unsplit(num_splits):
     np.testing.assert_allclose(lse_s, lse, rtol=1e-13, atol=1e-13)
 
 
+def test_combine_closed_forms():
+    # two partitions with equal normalisers: the plain mean, and lse + ln 2
+    o1, o2 = np.array([[1.0, -2.0]]), np.array([[3.0, 4.0]])
+    lse = np.array([0.7])
+    o, l = oracle.combine_partials(np.stack([o1, o2]), np.stack([lse, lse]))
+    np.testing.assert_allclose(o, (o1 + o2) / 2, rtol=1e-15)
+    np.testing.assert_allclose(l, lse + math.log(2.0), rtol=1e-15)
+    # a partition with no keys (lse = -inf) has zero weight, whatever its
+    # (finite) output
+    o3 = np.array([[1e30, -7.0]])
+    o, l = oracle.combine_partials(np.stack([o1, o3]), np.stack([lse, np.array([-np.inf])]))
+    np.testing.assert_array_equal(o, o1)
+    np.testing.assert_array_equal(l, lse)
+    # weights follow exp(lse_p): a partition e^5 times heavier dominates by that factor
+    o, l = oracle.combine_partials(np.stack([o1, o2]), np.stack([lse, lse + 5.0]))
+    w = math.exp(5.0)
+    np.testing.assert_allclose(o, (o1 + w * o2) / (1 + w), rtol=1e-14)
+    np.testing.assert_allclose(l, lse + math.log1p(w), rtol=1e-14)
+
+
+def test_combine_is_order_free():
+    rng = np.random.default_rng(27)
+    o_p, lse_p = rng.standard_normal((5, 3, 4)), 4 * rng.standard_normal((5, 3))
+    o, l = oracle.combine_partials(o_p, lse_p)
+    perm = rng.permutation(5)
+    o2, l2 = oracle.combine_partials(o_p[perm], lse_p[perm])
+    np.testing.assert_allclose(o2, o, rtol=1e-13)
+    np.testing.assert_allclose(l2, l, rtol=1e-14)
+
+
 def test_split_below_one_raises():
     rng = np.random.default_rng(26)
     with pytest.raises(ValueError):
