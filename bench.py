@@ -83,11 +83,16 @@ def decode_bytes(w) -> tuple[int, int]:
 
 
 def kernel_sources_digest() -> str:
-    """Digest of the library sources with comments and whitespace removed, so
-    that only a change to the code itself invalidates recorded counters."""
+    """Digest of the device sources (the kernels, their launch rules and the
+    headers they share: every .hip and .hpp file) with comments and whitespace
+    removed, so that only a change to kernel code invalidates recorded
+    counters.  The host-side argument checks (.cpp) run before any launch and
+    do not enter it; which kernel a call reaches is checked by name."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "io_aware_exact_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
+        if not f.endswith((".hip", ".hpp")):
+            continue
         with open(os.path.join(csrc, f), encoding="utf-8") as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -97,9 +102,10 @@ def kernel_sources_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel_prefix: str, workload: str):
+def measured_traffic(kernel_prefix: str, workload: str, kernel: str):
     """HBM bytes per launch from committed rocprofv3 counter summaries, only if
-    they were taken on the current kernel sources; otherwise None."""
+    they were taken on the current device sources and on the kernel that ran
+    (`kernel`, as attn_last_kernel names it); otherwise None."""
     path = os.path.join(PROFILES, "traffic.json")
     if not os.path.exists(path):
         return None
@@ -107,7 +113,7 @@ def measured_traffic(kernel_prefix: str, workload: str):
         with open(path) as f:
             rec = json.load(f)
         e = rec.get(workload, {}).get(kernel_prefix)
-        if not e or e.get("sources_sha256_16") != kernel_sources_digest():
+        if not e or e.get("sources_sha256_16") != kernel_sources_digest() or e.get("kernel") != kernel:
             return None
         return int(e["fetch_bytes"] + e["write_bytes"])
     except (OSError, ValueError, KeyError, TypeError):
@@ -335,7 +341,7 @@ def run_decode(torch, attn, steps, warmup, name="decode"):
         "kernel": kern,
         "repeats": reps,
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": gbps / PEAK_HBM_GBPS, "traffic": measured_traffic("decode", name)},
+                     "frac": gbps / PEAK_HBM_GBPS, "traffic": measured_traffic("decode", name, kern)},
         "parity": {"max_abs_err_o": max(errs_o), "max_abs_err_lse": max(errs_l), "heads_checked": len(errs_o)},
         "cpu_baseline": {"value": cpu_gbps, "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
                          "sample": f"{sample_heads} (batch, query head) slices, float64 numpy definition"},
@@ -371,7 +377,7 @@ def run_prefill(torch, attn, steps, warmup, name):
         "ms_per_step": ms,
         "kernel": kern,
         "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tf / PEAK_BF16_TFLOPS, "traffic": measured_traffic("prefill", name)},
+                     "frac": tf / PEAK_BF16_TFLOPS, "traffic": measured_traffic("prefill", name, kern)},
     }
 
 
@@ -415,7 +421,7 @@ def run_backward(torch, attn, steps, warmup, name="gpt2"):
         "ms_per_step": ms,
         "kernel": kern,
         "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tf / PEAK_BF16_TFLOPS, "traffic": measured_traffic("backward", name)},
+                     "frac": tf / PEAK_BF16_TFLOPS, "traffic": measured_traffic("backward", name, kern)},
         "parity": {"max_abs_err_dq_dk_dv": max(errs), "heads_checked": len(errs)},
     }
 
@@ -457,7 +463,7 @@ def run_prefill_split(torch, attn, steps, warmup, name="long_1head"):
         "speedup_vs_unsplit": ms_plain / ms,
         "max_abs_diff_vs_unsplit_o": diff,
         "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tf / PEAK_BF16_TFLOPS, "traffic": measured_traffic("prefill_split", name)},
+                     "frac": tf / PEAK_BF16_TFLOPS, "traffic": measured_traffic("prefill_split", name, kern)},
     }
 
 
@@ -521,7 +527,7 @@ def main():
     else:
         roof = {"bound": compute_bound, "achieved": tflops, "peak": compute_peak, "unit": "TFLOP/s",
                 "frac": tflops / compute_peak}
-    roof["traffic"] = measured_traffic("prefill", w.name)
+    roof["traffic"] = measured_traffic("prefill", w.name, kern)
     log(f"[bench] prefill {kern}: {ms * 1e3:.2f} us/step, {tflops:.1f} TFLOP/s")
     cold = None
     if not args.no_cold:

@@ -52,7 +52,8 @@ enum {
     ATTN_OK = 0,
     ATTN_EINVAL = -1,       /* null pointer, size < 1, scale not finite or <= 0, causal with T_q > T_kv,
                                pointer not 16-byte aligned, num_splits < 0, aliasing output, sizes overflow */
-    ATTN_EUNSUPPORTED = -2, /* head width d not built for this path */
+    ATTN_EUNSUPPORTED = -2, /* head width d not built for this path, or one head's K/V (or Q) past
+                               2^31 bytes, the reach of a 32-bit buffer range */
     ATTN_EHIP = -3,         /* the HIP runtime reported an error while enqueueing */
     ATTN_EWORKSPACE = -4    /* workspace missing or smaller than the call's *_workspace_bytes() */
 };
@@ -73,9 +74,9 @@ enum {
  * Those two roundings, each at most 2^-8 relative, bound every element:
  * |O - O_exact| <= 2^-8 (|O_exact| + A) plus fp32 rounding, where A is the
  * attention output with |V| as values (so at most 2^-7 max|V| for a row).
- * Supported: d in {64, 128} (64- and 32-key blocks); for T_q == 1 the decode
- * kernel runs unsplit (no workspace).  T_q and T_kv need not be multiples of
- * any tile.
+ * Supported: d in {64, 128} (64- and 32-key blocks), Tkv*d*2 < 2^31 bytes per
+ * head; for T_q == 1 the decode kernel runs unsplit (no workspace).  T_q and
+ * T_kv need not be multiples of any tile.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int Tq, int Tkv, int d, int causal, float scale, hipStream_t stream);
@@ -222,7 +223,7 @@ size_t attn_bwd_workspace_bytes(int B, int H, int Tq);
  * fp32 accumulation; P and dS are rounded to bf16 as MFMA operands.
  * Errors: as attn_fwd, plus ATTN_EINVAL for NULL dout/lse/dq/dk/dv or
  * overlapping buffers, ATTN_EWORKSPACE for a missing or small workspace.
- * Supported: d in {64, 128}.
+ * Supported: d in {64, 128}, Tq*d*2 and Tkv*d*2 < 2^31 bytes per head.
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
              float* dq, float* dk, float* dv, int B, int H, int Tq, int Tkv, int d, int causal, float scale,

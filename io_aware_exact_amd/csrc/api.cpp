@@ -137,6 +137,9 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
 int check_fwd_shape(int B, int H, int Tq, int Tkv, int d) {
     if (Tq == 1) {
         if (d != 64 && d != 128) return fail(ATTN_EUNSUPPORTED, "bf16 single-query path supports d in {64, 128}");
+        // the decode kernel it runs on has the same 32-bit buffer ranges per head
+        if (double(Tkv) * d * 2 >= 2147483648.0)
+            return fail(ATTN_EUNSUPPORTED, "bf16 single-query path supports Tkv*d*2 < 2^31 bytes per head");
         return ATTN_OK;
     }
     if (!attn::prefill_bf16_supports(d)) return fail(ATTN_EUNSUPPORTED, "bf16 prefill supports d in {64, 128}");

@@ -239,6 +239,11 @@ def test_largest_heads_are_bounded():
     big = (1 << 31) // (2 * 64)          # keys at d = 64 reaching exactly 2^31 bytes
     assert fwd(lib := attn.lib(), Tkv=big, Tq=64, causal=0) == EUNSUP and "2^31" in attn.attn_status_string(EUNSUP)
     assert fwd(lib, Tkv=big - 1, Tq=64, causal=0, q=0) == EINVAL    # the size itself is accepted (fails on q)
+    # a single query row takes the decode kernel, which has the same limit
+    assert fwd(lib, Tkv=big, Tq=1, causal=0) == EUNSUP and "2^31" in attn.attn_status_string(EUNSUP)
+    assert fwd(lib, Tkv=big, Tq=1, causal=1) == EUNSUP
+    assert fwd(lib, Tkv=big - 1, Tq=1, causal=0, q=0) == EINVAL
+    assert fsplit(lib, B=1, H=1, Tkv=big, Tq=1, causal=0) == EUNSUP
     assert fsplit(lib, B=1, H=1, Tkv=big, Tq=64, causal=0) == EUNSUP
     assert dec(lib, B=1, H=1, Tkv=(1 << 31) // 256) == EUNSUP
     assert bwd(lib, B=1, H=1, Tkv=big, causal=0) == EUNSUP

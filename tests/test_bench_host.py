@@ -2,8 +2,8 @@
 
 The refusal of more than one GPU, the algorithmic flop and byte counts the
 roofline divides by (against the cost model and brute force), the digest of
-the kernel sources, and the rule that recorded HBM traffic is reported only
-while it was taken on the current sources.
+the device sources, and the rule that recorded HBM traffic is reported only
+while it was taken on the current device sources and on the kernel that ran.
 """
 
 import importlib.util
@@ -91,17 +91,32 @@ def test_digest_ignores_comments_not_code(tmp_path, monkeypatch):
 
 def test_traffic_reported_only_for_current_sources(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
-    assert bench.measured_traffic("prefill", "gpt2") is None          # no record
-    rec = {"gpt2": {"prefill": {"sources_sha256_16": bench.kernel_sources_digest(),
+    kern = "prefill_bf16_d64<waves=4,bq=64,bk=64,key_halves=2,stages=2,causal>"
+    assert bench.measured_traffic("prefill", "gpt2", kern) is None          # no record
+    rec = {"gpt2": {"prefill": {"sources_sha256_16": bench.kernel_sources_digest(), "kernel": kern,
                                 "fetch_bytes": 1000.4, "write_bytes": 24.0}}}
     with open(os.path.join(tmp_path, "traffic.json"), "w") as f:
         json.dump(rec, f)
-    assert bench.measured_traffic("prefill", "gpt2") == 1024
-    assert bench.measured_traffic("decode", "gpt2") is None
+    assert bench.measured_traffic("prefill", "gpt2", kern) == 1024
+    assert bench.measured_traffic("decode", "gpt2", kern) is None
+    # counted on another kernel than the one that ran
+    assert bench.measured_traffic("prefill", "gpt2", kern.replace("stages=2", "stages=3")) is None
     rec["gpt2"]["prefill"]["sources_sha256_16"] = "0" * 16
     with open(os.path.join(tmp_path, "traffic.json"), "w") as f:
         json.dump(rec, f)
-    assert bench.measured_traffic("prefill", "gpt2") is None          # taken on other sources
+    assert bench.measured_traffic("prefill", "gpt2", kern) is None          # taken on other sources
+
+
+def test_digest_covers_device_code_only(tmp_path, monkeypatch):
+    csrc = copy_sources(str(tmp_path))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    base = bench.kernel_sources_digest()
+    with open(os.path.join(csrc, "api.cpp"), "a") as f:          # host-side checks
+        f.write("\nstatic int extra_check = 1;\n")
+    assert bench.kernel_sources_digest() == base
+    with open(os.path.join(csrc, "common.hpp"), "a") as f:       # shared by the kernels
+        f.write("\nstatic int extra_symbol = 1;\n")
+    assert bench.kernel_sources_digest() != base
 
 
 def test_committed_counters_were_taken_on_these_sources():
