@@ -377,6 +377,35 @@ def test_misaligned_view_rejected_before_launch():
         attn.attn_fwd(q, k, k)
 
 
+def test_wrong_output_shapes_rejected_before_launch():
+    """Outputs the caller passes must have exactly the shape the call writes;
+    a smaller buffer is refused in the binding, before any launch."""
+    q = torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16, device="cuda")
+    o_small = torch.empty(1, 2, 63, 64, dtype=torch.bfloat16, device="cuda")
+    lse_small = torch.empty(1, 2, 63, dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError, match="o must have shape"):
+        attn.attn_fwd(q, q, q, out=o_small)
+    with pytest.raises(ValueError, match="lse must have shape"):
+        attn.attn_fwd(q, q, q, lse=lse_small)
+    with pytest.raises(ValueError, match="o must have shape"):
+        attn.prepared_fwd(q, q, q, o_small, None, False)
+    with pytest.raises(ValueError, match="o must have shape"):
+        attn.attn_fwd_f32(q.float(), q.float(), q.float(), out=o_small.float())
+    lse = torch.empty(1, 2, 64, dtype=torch.float32, device="cuda")
+    d_small = torch.empty(1, 2, 64, 32, dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError, match="dk must have shape"):
+        attn.attn_bwd(q, q, q, q, lse, q, dk=d_small)
+    with pytest.raises(ValueError, match="lse must have shape"):
+        attn.attn_bwd(q, q, q, q, lse_small, q)
+    qd = torch.zeros(2, 4, 1, 64, dtype=torch.bfloat16, device="cuda")
+    kd = torch.zeros(2, 4, 100, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="lse must have shape"):
+        attn.attn_decode(qd, kd, kd, lse=torch.empty(2, 3, dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError, match="workspace must be a GPU tensor"):
+        attn.attn_decode(qd, kd, kd, num_splits=4, workspace=torch.empty(1 << 20, dtype=torch.uint8))
+    torch.cuda.synchronize()
+
+
 def test_no_device_allocation_during_call():
     """The score matrix never exists: a prefill call allocates nothing on the
     device beyond the caller's O and LSE (the library has no allocator)."""
