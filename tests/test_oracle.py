@@ -7,7 +7,9 @@ Python loops on tiny inputs, and PyTorch's CPU attention in float64.
 
 ``PIN_CHECKS`` below is also run against deliberately broken copies of the
 oracle (a dropped scale, transposed operands, a softmax over the wrong axis,
-a flipped causal mask, ...) to show that each plausible mistake is caught.
+a flipped causal mask, ...) to show that each plausible mistake is caught;
+``MORE_MUTANTS`` does the same for the blockwise recurrence, the one-query
+online form, the partition merge, the split and the grouped-query mapping.
 """
 
 import json
@@ -515,3 +517,198 @@ def test_gqa_rejects_uneven_groups():
     rng = np.random.default_rng(32)
     with pytest.raises(ValueError):
         oracle.attention_gqa(_rand(rng, 1, 6, 1, 4), _rand(rng, 1, 4, 5, 4), _rand(rng, 1, 4, 5, 4), 0.5)
+
+
+def test_combine_is_shift_invariant():
+    """Adding c to every partition's log-sum-exp scales every weight by e^c:
+    the merged output is unchanged and the merged LSE moves by c, also where
+    e^lse itself is past the float64 range (scores of a few hundred)."""
+    rng = np.random.default_rng(28)
+    o_p, lse_p = rng.standard_normal((4, 3, 5)), rng.standard_normal((4, 3))
+    o, l = oracle.combine_partials(o_p, lse_p)
+    eps = np.finfo(np.float64).eps
+    for c in (-900.0, 750.0, 1e4):
+        o2, l2 = oracle.combine_partials(o_p, lse_p + c)
+        assert np.isfinite(o2).all() and np.isfinite(l2).all(), c
+        # lse_p + c rounds at |c| eps / 2 absolute, so each weight carries a
+        # relative error up to about |c| eps (two such roundings per ratio)
+        tol = 4 * abs(c) * eps * np.abs(o_p).max() + 1e-14
+        np.testing.assert_allclose(o2, o, rtol=0, atol=tol)
+        np.testing.assert_allclose(l2, l + c, rtol=0, atol=4 * abs(c) * eps + 1e-14)
+
+
+# ------------------------------------------- planted mistakes beyond attention()
+#
+# Copies of the recurrence, the one-query online form, the partition merge, the
+# split and the grouped-query mapping, each with one plausible mistake.  Each is
+# installed in place of the original (in the package and in its defining
+# module, so internal callers see it too) and must fail at least one of the
+# pins above.
+
+_ATT = __import__("sys").modules["oracle.attention"]
+
+
+def _mut_states_no_rescale(scores, block):
+    s = np.asarray(scores, dtype=np.float64).ravel()
+    m, l, out = -math.inf, 0.0, []
+    for i in range(0, s.size, block):
+        sb = s[i:i + block]
+        m_new = max(m, float(sb.max()))
+        l = l + float(np.exp(sb - m_new).sum())          # old sum not rescaled
+        m = m_new
+        out.append((m, l))
+    return out
+
+
+def _mut_states_inverted_rescale(scores, block):
+    s = np.asarray(scores, dtype=np.float64).ravel()
+    m, l, out = -math.inf, 0.0, []
+    for i in range(0, s.size, block):
+        sb = s[i:i + block]
+        m_new = max(m, float(sb.max()))
+        l = (l * math.exp(m_new - m) if l else 0.0) + float(np.exp(sb - m_new).sum())
+        m = m_new
+        out.append((m, l))
+    return out
+
+
+def _mut_states_block_max_only(scores, block):
+    s = np.asarray(scores, dtype=np.float64).ravel()
+    m, l, out = -math.inf, 0.0, []
+    for i in range(0, s.size, block):
+        sb = s[i:i + block]
+        m_new = float(sb.max())                          # running max forgotten
+        l = l * math.exp(m - m_new) + float(np.exp(sb - m_new).sum())
+        m = m_new
+        out.append((m, l))
+    return out
+
+
+def _online_variant(rescale_acc=True, rescale_sum=True, scaled=True):
+    def online(q, K, V, block):
+        if block < 1:
+            raise ValueError("block must be at least 1")
+        q, K, V = (np.asarray(x, dtype=np.float64) for x in (q, K, V))
+        scale = 1.0 / math.sqrt(q.shape[0]) if scaled else 1.0
+        m, l, acc = -math.inf, 0.0, np.zeros(V.shape[1])
+        for i in range(0, K.shape[0], block):
+            s = (K[i:i + block] @ q) * scale
+            m_new = max(m, float(s.max()))
+            r = math.exp(m - m_new)
+            e = np.exp(s - m_new)
+            l = (l * r if rescale_sum else l) + float(e.sum())
+            acc = (acc * r if rescale_acc else acc) + e @ V[i:i + block]
+            m = m_new
+        return acc / l
+    return online
+
+
+def _mut_combine_mean(o_parts, lse_parts):
+    o_parts, lse_parts = np.asarray(o_parts, np.float64), np.asarray(lse_parts, np.float64)
+    M = lse_parts.max(axis=0)
+    return o_parts.mean(axis=0), M + np.log(np.exp(lse_parts - M[None]).sum(axis=0))
+
+
+def _mut_combine_lse_is_max(o_parts, lse_parts):
+    o, _ = oracle.attention_module_combine(o_parts, lse_parts)
+    return o, np.asarray(lse_parts, np.float64).max(axis=0)
+
+
+def _mut_combine_unshifted(o_parts, lse_parts):
+    o_parts, lse_parts = np.asarray(o_parts, np.float64), np.asarray(lse_parts, np.float64)
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        w = np.exp(lse_parts)                            # no max subtracted
+        wsum = w.sum(axis=0)
+        return (w[..., None] * o_parts).sum(axis=0) / wsum[..., None], np.log(wsum)
+
+
+def _mut_combine_divides_by_count(o_parts, lse_parts):
+    o_parts, lse_parts = np.asarray(o_parts, np.float64), np.asarray(lse_parts, np.float64)
+    M = lse_parts.max(axis=0)
+    w = np.exp(lse_parts - M[None])
+    return (w[..., None] * o_parts).sum(axis=0) / lse_parts.shape[0], M + np.log(w.sum(axis=0))
+
+
+def _split_variant(shift_hi=0, shift_lo=0):
+    def split(q, k, v, scale, num_splits):
+        if num_splits < 1:
+            raise ValueError("num_splits must be at least 1")
+        k, v = np.asarray(k, np.float64), np.asarray(v, np.float64)
+        tkv = k.shape[-2]
+        o_parts, lse_parts = [], []
+        for p in range(num_splits):
+            lo = max(0, (p * tkv) // num_splits + (shift_lo if p else 0))
+            hi = ((p + 1) * tkv) // num_splits + (shift_hi if p < num_splits - 1 else 0)
+            if hi <= lo:
+                continue
+            o_p, lse_p = attention(q, k[..., lo:hi, :], v[..., lo:hi, :], scale)
+            o_parts.append(o_p)
+            lse_parts.append(lse_p)
+        return _ATT.combine_partials(np.stack(o_parts), np.stack(lse_parts))
+    return split
+
+
+def _mut_gqa_modulo(q, k, v, scale, causal=False, rows=None):
+    q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+    hq, hkv = q.shape[1], k.shape[1]
+    if hq % hkv:
+        raise ValueError("H_q must be a multiple of H_kv")
+    outs = [attention(q[:, h], k[:, h % hkv], v[:, h % hkv], scale, causal, rows) for h in range(hq)]
+    return np.stack([o for o, _ in outs], axis=1), np.stack([l for _, l in outs], axis=1)
+
+
+_RECURRENCE_PINS = [
+    test_worked_example_after_block_1,
+    test_worked_example_final_state_equals_full_row,
+    test_worked_example_split_into_its_two_blocks,
+    lambda: test_blockwise_equals_full_for_every_block_size(7),
+    lambda: test_blockwise_equals_full_for_every_block_size(17),
+]
+_COMBINE_PINS = [
+    test_worked_example_split_into_its_two_blocks,
+    test_combine_closed_forms,
+    test_combine_is_order_free,
+    test_combine_is_shift_invariant,
+    lambda: test_split_combine_equals_unsplit(3),
+    lambda: test_split_combine_equals_unsplit(16),
+]
+_GQA_PINS = [test_gqa_with_one_query_head_per_group_is_attention, test_gqa_equals_attention_on_repeated_heads]
+
+MORE_MUTANTS = {  # name -> (function replaced, mutant, pins that must catch it)
+    "states_no_rescale": ("online_softmax_states", _mut_states_no_rescale, _RECURRENCE_PINS),
+    "states_inverted_rescale": ("online_softmax_states", _mut_states_inverted_rescale, _RECURRENCE_PINS),
+    "states_block_max_only": ("online_softmax_states", _mut_states_block_max_only, _RECURRENCE_PINS),
+    "online_acc_not_rescaled": ("online_attention", _online_variant(rescale_acc=False), _RECURRENCE_PINS),
+    "online_sum_not_rescaled": ("online_attention", _online_variant(rescale_sum=False), _RECURRENCE_PINS),
+    "online_unscaled_scores": ("online_attention", _online_variant(scaled=False), _RECURRENCE_PINS),
+    "combine_plain_mean": ("combine_partials", _mut_combine_mean, _COMBINE_PINS),
+    "combine_lse_is_max": ("combine_partials", _mut_combine_lse_is_max, _COMBINE_PINS),
+    "combine_unshifted_weights": ("combine_partials", _mut_combine_unshifted, _COMBINE_PINS),
+    "combine_divides_by_count": ("combine_partials", _mut_combine_divides_by_count, _COMBINE_PINS),
+    "split_drops_last_key": ("split_attention", _split_variant(shift_hi=-1), _COMBINE_PINS),
+    "split_overlapping_partitions": ("split_attention", _split_variant(shift_lo=-1), _COMBINE_PINS),
+    "gqa_modulo_heads": ("attention_gqa", _mut_gqa_modulo, _GQA_PINS),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MORE_MUTANTS))
+def test_pins_reject_planted_mistake_beyond_attention(name, monkeypatch):
+    target, mutant, pins = MORE_MUTANTS[name]
+    # the combine mutant that keeps the original output needs the original
+    monkeypatch.setattr(oracle, "attention_module_combine", _ATT.combine_partials, raising=False)
+    monkeypatch.setattr(oracle, target, mutant)
+    monkeypatch.setattr(_ATT, target, mutant)
+    caught = 0
+    for pin in pins:
+        try:
+            pin()
+        except Exception:          # an assertion, or a failure inside the mutant
+            caught += 1
+    assert caught, f"mutant {name} passed every pin"
+
+
+def test_unmutated_pins_pass():
+    """The same pin lists, run on the oracle as it is, all pass (so that a
+    mutant counts as caught only by its mistake)."""
+    for pin in _RECURRENCE_PINS + _COMBINE_PINS + _GQA_PINS:
+        pin()
