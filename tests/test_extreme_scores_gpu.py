@@ -190,3 +190,55 @@ def test_patterns_span_past_the_exponent_range():
     assert abs(np.abs(s).max() - SPAN) < 0.01 * SPAN
     rising = s[0]
     assert (rising[-64:].max() - rising[:64].max()) / math.log(2.0) > 128
+
+
+@gpu
+@pytest.mark.parametrize("B,H,Tq,Tkv,d,causal", [
+    (1, 4, 300, 300, 64, False), (1, 4, 300, 300, 64, True), (2, 4, 1000, 1000, 64, True),
+    (1, 4, 300, 300, 128, False), (1, 4, 257, 400, 128, True)])
+def test_extreme_backward(B, H, Tq, Tkv, d, causal):
+    """The backward takes O and LSE as inputs: both sides get the GPU forward's
+    bf16 O and fp32 LSE (|LSE| up to 600), so P = exp(s * scale - LSE) is
+    recomputed from the same numbers.
+
+    Bar, per element: |g_gpu - g| <= 2^-8 (|g| + A) (1 + 2^-6) + E + 1e-6 max|g|.
+    The kernels round P (for dV) and dS = P (dP - D) (for dQ and dK) to bf16,
+    2^-9 relative per term; A sums the terms of each product in absolute
+    value: scale |dS| |K| for dQ, scale |dS|^T |Q| for dK, |P|^T |dO| for dV.
+    E carries the fp32 error of dP - D, which two different summations of d
+    products form (a d-term sum errs by at most d 2^-24 sum|terms|), through
+    the same products: scale (P e) |K| for dQ, scale (P e)^T |Q| for dK.
+    Where P is one-hot and O is that key's V, dP - D is 0 exactly and only
+    this residue remains.  With |k| up to 75 here, dQ sums large terms that
+    nearly cancel, which a bar relative to max|dQ| (the ordinary backward
+    cases') does not cover."""
+    scale = d ** -0.5
+    say(f"case extreme backward B={B} H={H} Tq={Tq} Tkv={Tkv} d={d} causal={causal}")
+    q, k, v = extreme_qkv(B, H, H, Tq, Tkv, d, scale, "bf16", 46)
+    do = make_tensor(47, "v", B, H, Tq, d, "bf16")
+    qc, kc, vc, doc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = attn.attn_fwd(qc, kc, vc, causal=causal, scale=scale)
+    gq, gk, gv = attn.attn_bwd(qc, kc, vc, o, lse, doc, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    say(f"  {attn.attn_last_kernel()}")
+    Q, K, V, O, dO, L = (to_f64(t) for t in (q, k, v, o, do, lse))
+    refs = oracle.attention_backward_from_lse(Q, K, V, O, dO, L, scale, causal)
+    # magnitudes of the terms each gradient sums (for the rounding bound only)
+    s_ = scale * (Q @ np.swapaxes(K, -1, -2))
+    if causal:
+        s_ = np.where(np.arange(Tkv)[None, :] > np.arange(Tq)[:, None] + (Tkv - Tq), -np.inf, s_)
+    P = np.exp(s_ - L[..., None])
+    dS = P * (dO @ np.swapaxes(V, -1, -2) - (dO * O).sum(-1)[..., None])
+    e32 = d * 2.0 ** -24 * (np.abs(dO) @ np.swapaxes(np.abs(V), -1, -2) + (np.abs(dO) * np.abs(O)).sum(-1)[..., None])
+    Pe = P * e32
+    A = {"dQ": scale * (np.abs(dS) @ np.abs(K)), "dK": scale * (np.swapaxes(np.abs(dS), -1, -2) @ np.abs(Q)),
+         "dV": np.swapaxes(P, -1, -2) @ np.abs(dO)}
+    E = {"dQ": scale * (Pe @ np.abs(K)), "dK": scale * (np.swapaxes(Pe, -1, -2) @ np.abs(Q)), "dV": 0.0}
+    for name, got, ref in zip(("dQ", "dK", "dV"), (gq, gk, gv), refs[:3]):
+        g = to_f64(got)
+        assert np.isfinite(g).all(), name
+        err = np.abs(g - ref)
+        bound = 2.0 ** -8 * (np.abs(ref) + A[name]) * (1 + 2.0 ** -6) + E[name] + 1e-6 * float(np.abs(ref).max())
+        ratio = float((err / bound).max())
+        say(f"  {name}: max|err| {err.max():.3e} max|ref| {float(np.abs(ref).max()):.3e} max err/bound {ratio:.3f}")
+        assert ratio <= 1.0, f"{name} error {err.max()} (err/bound {ratio})"
