@@ -84,7 +84,10 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 /*
  * attn_fwd_split_workspace_bytes -- bytes of workspace attn_fwd_split needs for
  * this shape and kv_chunk; 0 when that call would not split (then it needs no
- * workspace) or when the arguments are invalid.
+ * workspace) or when the arguments are invalid.  The workspace holds, per
+ * chunk of a split tile, the partial output and partial normaliser that
+ * "IO-Aware Attention", section "Parallelism and the cost of the split", has
+ * each key partition produce before the merge.  Caller-owned device memory.
  */
 size_t attn_fwd_split_workspace_bytes(int B, int H, int Tq, int Tkv, int d, int causal, int kv_chunk);
 
@@ -121,7 +124,12 @@ int attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* 
 
 /*
  * attn_fwd_f32 -- the exact path: fp32 inputs, fp32 products, fp32 output.
- * Same arguments and semantics as attn_fwd with every tensor fp32.
+ * Same arguments and semantics as attn_fwd with every tensor fp32: the same
+ * definition ("FlashAttention IO-aware tiling lab"; "Attention and Its
+ * Computational Cost", section "What is being computed") with the same
+ * blockwise recurrence, and no reduced-precision step anywhere, the 32-bit
+ * arithmetic "IO-Aware Attention", section "Where the approach stops
+ * helping", asks of the accumulation and rescaling.  Errors as attn_fwd.
  * Supported: d in {16, 32, 64, 128}, any T_q >= 1, T_kv >= 1.
  */
 int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
@@ -130,8 +138,9 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
 /*
  * attn_decode_workspace_bytes -- bytes of workspace attn_decode needs:
  * B*H*num_splits*(d+2)*4 (one fp32 partial output of d values plus its
- * running max and running sum per partition), 0 when num_splits <= 1 or any
- * size is < 1.
+ * running max and running sum per partition, the per-partition state of
+ * "IO-Aware Attention", section "Parallelism and the cost of the split"),
+ * 0 when num_splits <= 1 or any size is < 1.  Caller-owned device memory.
  */
 size_t attn_decode_workspace_bytes(int B, int H, int d, int num_splits);
 
@@ -194,8 +203,10 @@ int attn_decode_gqa(const void* q, const void* k, const void* v, void* o, float*
 
 /*
  * attn_bwd_workspace_bytes -- bytes of workspace attn_bwd needs: B*H*Tq*8
- * (per query row its log-sum-exp in base 2 and D = sum_d dO*O, fp32).
- * 0 when any size is < 1.
+ * (per query row its log-sum-exp in base 2 and D = sum_d dO*O, fp32: the O(n)
+ * row constants "IO-Aware Attention", section "What has to stay in fast
+ * memory", keeps beside the inputs).  0 when any size is < 1.  Caller-owned
+ * device memory.
  */
 size_t attn_bwd_workspace_bytes(int B, int H, int Tq);
 
