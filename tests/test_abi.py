@@ -271,3 +271,26 @@ def test_binding_rejects_host_tensors():
         attn.attn_fwd(x, x, x)
     with pytest.raises(ValueError, match="shape"):
         attn.attn_fwd(x, torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16), x)
+
+
+def test_prepared_call_refuses_another_current_device(monkeypatch):
+    """A prepared callable launches on the device current when it runs, so it
+    refuses to run unless that is the device its tensors live on (host logic
+    only: the current device is stubbed and the C call is a stand-in)."""
+    import torch
+    from io_aware_exact_amd import attn as binding
+
+    calls = []
+
+    def fake_entry(*args):
+        calls.append(args)
+        return attn.ATTN_OK
+
+    call = binding._prepared(fake_entry, (1, 2, 3), torch.device("cuda", 1))
+    monkeypatch.setattr(torch.cuda, "current_device", lambda: 0)
+    with pytest.raises(RuntimeError, match="cuda:0 is current"):
+        call()
+    assert calls == []
+    monkeypatch.setattr(torch.cuda, "current_device", lambda: 1)
+    call()
+    assert calls == [(1, 2, 3)]
