@@ -146,3 +146,65 @@ def test_mfma_probe_library_exports():
     assert lib.probe_mfma_loop_flops(2048, 4096) == 2048 * 4 * 4096 * 4 * 32768
     assert lib.probe_mfma_loop(0, 1, None, None) != 0            # rejected before any launch
     assert lib.probe_mfma_loop(1, 1, None, None) != 0
+
+
+ROCMINFO_SAMPLE = """
+*******
+Agent 1
+*******
+  Name:                    Intel(R) Xeon(R) Platinum
+  Max Clock Freq. (MHz):   3800
+*******
+Agent 2
+*******
+  Name:                    gfx950
+  Marketing Name:          AMD Instinct MI355X
+  Max Clock Freq. (MHz):   2400
+"""
+
+
+def test_rocminfo_clock_is_the_gpu_agents():
+    assert bench.parse_rocminfo_clock(ROCMINFO_SAMPLE) == 2400
+    assert bench.parse_rocminfo_clock("Name: gfx950\n") is None
+    assert bench.parse_rocminfo_clock("") is None
+
+
+def test_roofline_bound_follows_the_longer_time():
+    # gpt2: 25.4 MB at 8 TB/s (3.17 us) outlasts 6.45 GFLOP at 2.5 PFLOP/s (2.58 us)
+    r = bench.prefill_roofline(WORKLOADS["gpt2"], 0.01)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s"
+    assert r["achieved"] == pytest.approx(25_362_432 / 1e-5 / 1e9)
+    assert r["frac"] == pytest.approx(r["achieved"] / 8000.0)
+    for name in ("mid", "mid_causal", "long"):
+        r = bench.prefill_roofline(WORKLOADS[name], 1.0)
+        assert r["bound"] == "mfma" and r["peak"] == 2500.0
+        assert r["achieved"] == pytest.approx(bench.prefill_flops(WORKLOADS[name]) / 1e-3 / 1e12)
+    assert bench.prefill_roofline(WORKLOADS["tiny"], 1.0)["bound"] == "alu"
+
+
+def test_headline_is_the_long_prefill():
+    w = WORKLOADS[bench.HEADLINE]
+    assert (w.B, w.H, w.Tq, w.Tkv, w.d, w.causal, w.dtype) == (1, 12, 16384, 16384, 64, True, "bf16")
+    assert bench.prefill_flops(w) == 412_342_026_240          # 4 * 12 * 64 * 16384 * 16385 / 2
+
+
+def test_leg_selection():
+    import argparse
+    ns = argparse.Namespace(no_decode=False, no_split=False, no_extra=False, no_backward=False)
+    assert bench.parse_legs("all", ns) == list(bench.LEGS)
+    assert bench.parse_legs("none", ns) == []
+    assert bench.parse_legs("mid,mid_causal", ns) == ["mid", "mid_causal"]
+    ns.no_decode = True
+    assert not set(bench.parse_legs("all", ns)) & set(bench.DECODE_LEGS)
+    with pytest.raises(SystemExit):
+        bench.parse_legs("mid,nonsense", ns)
+
+
+def test_sampled_rows_cover_edges_and_stay_in_range():
+    import numpy as np
+    rows = bench.sampled_rows(16384, 512, np.random.default_rng(0))
+    assert rows.min() == 0 and rows.max() == 16383
+    assert len(set(rows.tolist())) == rows.size >= 512
+    assert {127, 128, 129, 16255, 16256} <= set(rows.tolist())
+    small = bench.sampled_rows(40, 512, np.random.default_rng(0))
+    assert small.tolist() == list(range(40))
