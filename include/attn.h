@@ -202,6 +202,35 @@ int attn_decode_gqa(const void* q, const void* k, const void* v, void* o, float*
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * attn_decode_noalloc -- attn_decode_gqa for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the partition partials go to a scratch array the
+ * library holds on each device (one per device, kept until the process ends)
+ * instead of a caller workspace.  The call allocates and frees nothing.
+ *
+ *   arguments  as attn_decode_gqa, without the workspace
+ *
+ * Limit: the partials, attn_decode_workspace_bytes(B,Hq,d,P) for the
+ * partition count P actually used (after num_splits == 0 is resolved and
+ * clamped to Tkv), must fit in attn_decode_noalloc_max_bytes() (32 MiB);
+ * a larger call returns ATTN_EWORKSPACE before any launch.  P == 1 uses no
+ * scratch.  The scratch's address on a device is looked up on the first
+ * call made with that device current.
+ * Every call on one device shares its scratch: two calls that may run at
+ * the same time on one device (different streams, or host threads without an
+ * order between them) race on it and give wrong results; order them on one
+ * stream.  Each call overwrites every record it later reads, so nothing needs
+ * clearing between calls.  Errors: as attn_decode_gqa, plus ATTN_EHIP when the
+ * scratch address cannot be obtained.
+ */
+int attn_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int Hq, int Hkv, int Tkv, int d, float scale, int num_splits,
+                        hipStream_t stream);
+
+/* attn_decode_noalloc_max_bytes -- size of that per-device scratch (32 MiB). */
+size_t attn_decode_noalloc_max_bytes(void);
+
+/*
  * attn_bwd_workspace_bytes -- bytes of workspace attn_bwd needs: B*H*Tq*8
  * (per query row its log-sum-exp in base 2 and D = sum_d dO*O, fp32: the O(n)
  * row constants "IO-Aware Attention", section "What has to stay in fast

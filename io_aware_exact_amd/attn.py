@@ -39,6 +39,8 @@ SIGNATURES = {
     "attn_decode_splits": (_I, [_I, _I, _I, _I, _I]),
     "attn_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _S, _P]),
     "attn_decode_gqa": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _S, _P]),
+    "attn_decode_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_decode_noalloc_max_bytes": (_S, []),
     "attn_bwd_workspace_bytes": (_S, [_I, _I, _I]),
     "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _S, _P]),
     "attn_last_kernel": (ctypes.c_char_p, []),
@@ -272,6 +274,26 @@ def attn_decode_gqa(q, k, v, scale: float | None = None, num_splits: int = 16, w
         st = lib().attn_decode_gqa(*ptrs, lp, B, Hq, Hkv, Tkv, d, scale, int(num_splits), wp, wbytes, _stream(dev))
     _check(st)
     return (o, lse) if return_lse else o
+
+
+def attn_decode_noalloc_max_bytes() -> int:
+    return int(lib().attn_decode_noalloc_max_bytes())
+
+
+def attn_decode_noalloc(q, k, v, o, lse=None, scale: float | None = None, num_splits: int = 16):
+    """attn_decode_gqa writing its partials to the library's per-device
+    scratch instead of a workspace: nothing is allocated, here or in the
+    library, so the caller passes the outputs ``o`` [B,Hq,1,d] and
+    (optionally) ``lse`` [B,Hq].  Calls on one device must not overlap."""
+    B, Hq, Hkv, Tkv, d = _shape_gqa(q, k, v)
+    dev = _gpu(q)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    lp = _lse_ptr(lse, (B, Hq), dev)
+    ptrs = _qkvo(q, k, v, o, torch.bfloat16, dev)
+    with torch.cuda.device(dev):
+        st = lib().attn_decode_noalloc(*ptrs, lp, B, Hq, Hkv, Tkv, d, scale, int(num_splits), _stream(dev))
+    _check(st)
+    return o, lse
 
 
 def attn_bwd_workspace_bytes(B: int, H: int, Tq: int) -> int:

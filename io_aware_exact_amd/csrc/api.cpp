@@ -102,6 +102,24 @@ int run_decode(const void* q, const void* k, const void* v, void* o, float* lse,
     return finish(attn::launch_decode_bf16(a, stream, &name), name);
 }
 
+// Checks of a decode call (one query per (batch, query head)) and the
+// partition count it will use: num_splits, or the automatic count for 0,
+// clamped to Tkv.
+int check_decode(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int Hq,
+                 int Hkv, int Tkv, int d, float scale, int num_splits, int* splits) {
+    int st = check_common(q, k, v, o, lse, B, Hq, Hkv, 1, Tkv, d, 0, scale, 2);
+    if (st != ATTN_OK) return st;
+    if (num_splits < 0) return fail(ATTN_EINVAL, "num_splits must be >= 0");
+    if (d != 64 && d != 128) return fail(ATTN_EUNSUPPORTED, "decode supports d in {64, 128}");
+    // buffer-load ranges are 32-bit byte counts per (batch, kv head)
+    if (double(Tkv) * d * 2 >= 2147483648.0)
+        return fail(ATTN_EUNSUPPORTED, "decode supports Tkv*d*2 < 2^31 bytes per head");
+    if (num_splits == 0) num_splits = attn::decode_auto_splits(B, Hq, Hkv, Tkv, d);
+    *splits = num_splits > Tkv ? Tkv : num_splits;
+    if (*splits > 65535) return fail(ATTN_EUNSUPPORTED, "decode supports at most 65535 partitions");
+    return ATTN_OK;
+}
+
 // The workspace must be 16-byte aligned and overlap none of the tensors.
 int check_workspace(const void* ws, size_t need, const void* q, const void* k, const void* v, const void* o,
                     const float* lse, uint64_t qbytes, uint64_t kvbytes, uint64_t lsebytes) {
@@ -217,16 +235,9 @@ size_t attn_decode_workspace_bytes(int B, int H, int d, int num_splits) {
 int attn_decode_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
                     int Tkv, int d, float scale, int num_splits, void* workspace, size_t workspace_bytes,
                     hipStream_t stream) {
-    int st = check_common(q, k, v, o, lse, B, Hq, Hkv, 1, Tkv, d, 0, scale, 2);
+    int splits = 0;
+    int st = check_decode(q, k, v, o, lse, B, Hq, Hkv, Tkv, d, scale, num_splits, &splits);
     if (st != ATTN_OK) return st;
-    if (num_splits < 0) return fail(ATTN_EINVAL, "num_splits must be >= 0");
-    if (d != 64 && d != 128) return fail(ATTN_EUNSUPPORTED, "decode supports d in {64, 128}");
-    // buffer-load ranges are 32-bit byte counts per (batch, kv head)
-    if (double(Tkv) * d * 2 >= 2147483648.0)
-        return fail(ATTN_EUNSUPPORTED, "decode supports Tkv*d*2 < 2^31 bytes per head");
-    if (num_splits == 0) num_splits = attn::decode_auto_splits(B, Hq, Hkv, Tkv, d);
-    const int splits = num_splits > Tkv ? Tkv : num_splits;
-    if (splits > 65535) return fail(ATTN_EUNSUPPORTED, "decode supports at most 65535 partitions");
     if (splits > 1) {
         const size_t need = attn_decode_workspace_bytes(B, Hq, d, splits);
         if (!workspace) return fail(ATTN_EWORKSPACE, "workspace is NULL");
@@ -239,6 +250,28 @@ int attn_decode_gqa(const void* q, const void* k, const void* v, void* o, float*
     }
     return run_decode(q, k, v, o, lse, B, Hq, Hkv, Tkv, d, scale, splits, workspace, stream);
 }
+
+int attn_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                        int Tkv, int d, float scale, int num_splits, hipStream_t stream) {
+    int splits = 0;
+    int st = check_decode(q, k, v, o, lse, B, Hq, Hkv, Tkv, d, scale, num_splits, &splits);
+    if (st != ATTN_OK) return st;
+    void* scratch = nullptr;
+    if (splits > 1) {
+        const size_t need = attn_decode_workspace_bytes(B, Hq, d, splits);
+        if (need > attn::kDecodeScratchBytes)
+            return fail(ATTN_EWORKSPACE, "the partials need " + std::to_string(need) +
+                                             " bytes; the library's scratch holds " +
+                                             std::to_string(attn::kDecodeScratchBytes) +
+                                             " (use fewer splits, or attn_decode_gqa with a workspace)");
+        const hipError_t e = attn::decode_scratch(&scratch);
+        if (e != hipSuccess)
+            return fail(ATTN_EHIP, std::string("scratch lookup failed: ") + hipGetErrorString(e));
+    }
+    return run_decode(q, k, v, o, lse, B, Hq, Hkv, Tkv, d, scale, splits, scratch, stream);
+}
+
+size_t attn_decode_noalloc_max_bytes(void) { return attn::kDecodeScratchBytes; }
 
 int attn_decode_splits(int B, int Hq, int Hkv, int Tkv, int d) {
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Tkv < 1 || (d != 64 && d != 128)) return 0;

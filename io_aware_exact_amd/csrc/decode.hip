@@ -31,6 +31,7 @@
 // Partial record per (batch*query head, partition): o (D floats, not
 // normalised), then m (max of scale*log2e*q.k) and l, all fp32.
 #include <cstdio>
+#include <mutex>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -582,6 +583,37 @@ int decode_auto_splits(int B, int Hq, int Hkv, int Tkv, int d) {
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream, const char** name) {
     if (a.d == 128) return launch_d<128>(a, stream, name);
     return launch_d<64>(a, stream, name);
+}
+
+// Partial-record storage of the allocation-free decode entry point: one
+// array per device, part of the library's code object, held until the
+// process ends.  Host code never passes `scratch` itself to a kernel (on the
+// host that name is only a stand-in for the device symbol): it takes the
+// device address from hipGetSymbolAddress, once per device with that device
+// current, and hands that address to the kernels like a caller's workspace.
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 }  // namespace attn

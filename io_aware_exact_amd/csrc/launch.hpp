@@ -70,4 +70,9 @@ hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream, const
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream, const char** name);
 int decode_auto_splits(int B, int Hq, int Hkv, int Tkv, int d);
 
+// Size of the library's own per-device decode partials (32 MiB), and its
+// device address on the current device (looked up once per device).
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+hipError_t decode_scratch(void** ptr);
+
 }  // namespace attn

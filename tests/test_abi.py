@@ -150,6 +150,34 @@ def test_gqa_decode_arguments(lib):
     assert gqa(lib, ws=K + kv_bytes - 64) == EINVAL and "overlaps" in attn.attn_status_string(EINVAL)
 
 
+def noalloc(lib, **kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, Hq=8, Hkv=2, Tkv=100, d=128, scale=0.088, P=4, stream=None)
+    a.update(kw)
+    return lib.attn_decode_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Tkv"],
+                                   a["d"], a["scale"], a["P"], a["stream"])
+
+
+def test_noalloc_decode_arguments(lib):
+    cap = lib.attn_decode_noalloc_max_bytes()
+    assert cap == 32 << 20
+    assert noalloc(lib, Hkv=3) == EINVAL and "multiple of Hkv" in attn.attn_status_string(EINVAL)
+    assert noalloc(lib, q=None) == EINVAL
+    assert noalloc(lib, P=-1) == EINVAL
+    assert noalloc(lib, d=96) == EUNSUP
+    assert noalloc(lib, o=K + 64) == EINVAL and "o overlaps k" in attn.attn_status_string(EINVAL)
+    # partials past the scratch are refused before any device call: 64 x 32
+    # heads x 64 partitions x 130 floats = 68 MB, and the limit is exact
+    assert noalloc(lib, B=64, Hq=32, Hkv=32, Tkv=8192, P=64) == EWS
+    assert str(cap) in attn.attn_status_string(EWS)
+    assert attn.attn_decode_workspace_bytes(64, 32, 128, 64) > cap >= attn.attn_decode_workspace_bytes(64, 32, 128, 30)
+    # the partition count is clamped to Tkv before the size check: 64 keys at
+    # most 64 partitions, 4 keys at most 4
+    assert noalloc(lib, B=64, Hq=32, Hkv=32, Tkv=64, P=1000) == EWS
+    big = attn.attn_decode_workspace_bytes(1024, 32, 128, 4)
+    assert big > cap
+    assert noalloc(lib, B=1024, Hq=32, Hkv=32, Tkv=4, P=1000) == EWS and str(big) in attn.attn_status_string(EWS)
+
+
 def test_split_forward_arguments(lib):
     assert fsplit(lib, chunk=-1) == EINVAL and "kv_chunk" in attn.attn_status_string(EINVAL)
     assert fsplit(lib, ws=None) == EWS and "NULL" in attn.attn_status_string(EWS)
