@@ -724,6 +724,37 @@ def mfma_loop_rate(torch, blocks: int = 2048, iters: int = 4096):
 
 # ------------------------------------------------------------------ main
 
+def copy_calibration(torch) -> int:
+    """Three device-to-device copies of 512 MiB: a kernel of known traffic
+    that HBM byte counters are scaled by."""
+    src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    n = src.numel()
+    del src, dst
+    torch.cuda.empty_cache()
+    return n
+
+
+def run_leg(torch, attn, leg, args, cpu_seconds: float) -> dict:
+    if leg in PREFILL_LEGS:
+        return run_prefill(torch, attn, leg, args, cpu_seconds, cold=(leg == "gpt2"))
+    if leg in DECODE_LEGS:
+        r = run_decode(torch, attn, leg, args, cpu_seconds)
+        log(f"[bench] {leg} {r['kernel']}: {r['ms_per_step']:.3f} ms/step, {r['value']:.0f} GB/s")
+        return r
+    if leg == "backward":
+        r = run_backward(torch, attn, args)
+        log(f"[bench] backward {r['kernel']}: {r['ms_per_step'] * 1e3:.1f} us/step, {r['value']:.1f} TFLOP/s")
+        return r
+    r = run_prefill_split(torch, attn, args)
+    log(f"[bench] prefill_split {r['kernel']}: {r['ms_per_step'] * 1e3:.1f} us/step "
+        f"(unsplit {r['unsplit']['ms_per_step'] * 1e3:.1f} us)")
+    return r
+
+
 def parse_legs(spec: str, args) -> list:
     if spec in ("", "none"):
         legs = []
@@ -764,6 +795,8 @@ def main():
     ap.add_argument("--no-ceilings", action="store_true", help="skip the copy / GEMM / matrix-pipe ceilings")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle leg of the headline: seconds of CPU work")
     ap.add_argument("--leg-cpu-seconds", type=float, default=3.0, help="oracle leg of each other leg: seconds")
+    ap.add_argument("--legs-only", action="store_true",
+                    help="run only the legs (no headline line): for profiling one leg's kernels on their own")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 3 device-to-device copies of 512 MiB (a reference for HBM byte counters)")
     args = ap.parse_args()
@@ -790,6 +823,13 @@ def main():
     cpu_main = 0.0 if args.no_cpu_baseline else args.cpu_seconds
     cpu_leg = 0.0 if args.no_cpu_baseline else args.leg_cpu_seconds
 
+    if args.legs_only:
+        out = {"legs": {leg: run_leg(torch, attn, leg, args, cpu_leg) for leg in legs}}
+        if args.copy_calibration:
+            out["copy_calibration_bytes"] = copy_calibration(torch)
+        out["kernel_sources_digest"] = kernel_sources_digest()
+        print(json.dumps(out), flush=True)
+        return
     head = run_prefill(torch, attn, args.workload, args, cpu_main, cold=True)
     props = torch.cuda.get_device_properties(0)
     result = {
@@ -829,19 +869,7 @@ def main():
                              "scale": w.scale})
     result["legs"] = {}
     for leg in legs:
-        if leg in PREFILL_LEGS:
-            r = run_prefill(torch, attn, leg, args, cpu_leg, cold=(leg == "gpt2"))
-        elif leg in DECODE_LEGS:
-            r = run_decode(torch, attn, leg, args, cpu_leg)
-            log(f"[bench] {leg} {r['kernel']}: {r['ms_per_step']:.3f} ms/step, {r['value']:.0f} GB/s")
-        elif leg == "backward":
-            r = run_backward(torch, attn, args)
-            log(f"[bench] backward {r['kernel']}: {r['ms_per_step'] * 1e3:.1f} us/step, {r['value']:.1f} TFLOP/s")
-        else:
-            r = run_prefill_split(torch, attn, args)
-            log(f"[bench] prefill_split {r['kernel']}: {r['ms_per_step'] * 1e3:.1f} us/step "
-                f"(unsplit {r['unsplit']['ms_per_step'] * 1e3:.1f} us)")
-        result["legs"][leg] = r
+        result["legs"][leg] = run_leg(torch, attn, leg, args, cpu_leg)
     legs_run = result["legs"]
     if "mid" in legs_run and "mid_causal" in legs_run:
         t_full = legs_run["mid"]["repeats"]["median_ms"]
@@ -860,12 +888,7 @@ def main():
         log(f"[bench] achievable: copy {ceil['copy_GBps']:.0f} GB/s, bf16 GEMM {ceil['bf16_gemm_TFLOPs']:.0f} TFLOP/s,"
             f" MFMA loop {ceil.get('mfma_loop_TFLOPs', float('nan')):.0f} TFLOP/s")
     if args.copy_calibration:
-        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        result["copy_calibration_bytes"] = src.numel()
+        result["copy_calibration_bytes"] = copy_calibration(torch)
     result["kernel_sources_digest"] = kernel_sources_digest()
     print(json.dumps(result), flush=True)
 

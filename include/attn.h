@@ -282,7 +282,11 @@ const char* attn_last_kernel(void);
 /*
  * attn_status_string -- description of `status`; for the calling thread's most
  * recent failure with that code it carries the detail (which argument, or the
- * HIP error text).  Thread-local storage, valid until the next call.
+ * HIP error text).  Thread-local storage, valid until the next call.  This is
+ * the C form of the argument errors of "E8.1 IO-aware attention", "Do it in
+ * code" (a block size below 1 is refused with an error that says why): every
+ * entry point checks its arguments before touching the device and reports a
+ * refusal as a status code whose text names the argument.
  */
 const char* attn_status_string(int status);
 

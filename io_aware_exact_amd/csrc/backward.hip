@@ -1,10 +1,11 @@
 // Exact attention backward, bf16 inputs, head width 64 or 128, gfx950.
 //
-// The softmax output is not stored by the forward pass; it is recomputed here
-// from Q, K, V and the saved per-row log-sum-exp ("IO-Aware Attention:
-// Tiling the Score Matrix Without Materializing It", section "What has to
-// stay in fast memory": the recomputation is one more pass over the score
-// blocks, paid in flops instead of bytes).  With c = scale * log2 e,
+// The forward pass keeps O and one log-sum-exp per query row, not the
+// probabilities; they are rebuilt here block by block from Q, K, V and that
+// row value ("IO-Aware Attention: Tiling the Score Matrix Without
+// Materializing It", section "What has to stay in fast memory"): another
+// sweep of matrix products costs less than writing the T_q x T_kv
+// probabilities out and reading them back.  With c = scale * log2 e,
 // lse2 = lse * log2 e and D_i = sum_d dO_id O_id:
 //
 //   P  = exp2(c * Q K^T - lse2)         (recomputed per block, never stored)

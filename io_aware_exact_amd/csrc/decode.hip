@@ -1,10 +1,10 @@
 // Exact attention for one query per (batch, query head) against cached keys
 // and values (decode), bf16 inputs, head width 64 or 128, gfx950.
 //
-// With a single query row there is nothing to tile in the query dimension and
-// the work is a streaming reduction over the cache, bound by reading K and V
-// once ("IO-Aware Attention: Tiling the Score Matrix Without Materializing
-// It", section "Where the approach stops helping"; "Attention and Its
+// One query row per head leaves no query axis to block over: a step reads
+// every cached K and V row once and folds it into one output, so its time is
+// the time to read the cache ("IO-Aware Attention: Tiling the Score Matrix
+// Without Materializing It", section "Where the approach stops helping"; "Attention and Its
 // Computational Cost", section "The other shape: one query, many keys").
 // The key axis is split into P contiguous partitions, each reduced by its own
 // workgroup to a partial output and normaliser, and a second kernel merges the

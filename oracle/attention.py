@@ -133,28 +133,50 @@ def standard_attention(q, K, V):
     return (p @ V) / p.sum()
 
 
+def _block_summary(s, vb=None):
+    """One block's own softmax state, relative to its own maximum m_b: the
+    sum of exp(s_j - m_b) and (when values are given) the exp-weighted sum
+    of its value rows."""
+    m_b = float(s.max())
+    e = np.exp(s - m_b)
+    return m_b, float(e.sum()), (None if vb is None else e @ vb)
+
+
+def _rescale_merge(run, blk):
+    """The running state (m, l, acc) extended by a block's summary: both are
+    put on the common reference max(m, m_b), each side multiplied by
+    exp(its own reference - the common one).  An empty running state
+    (m = -inf) gets weight 0."""
+    m, l, acc = run
+    m_b, l_b, acc_b = blk
+    m_new = max(m, m_b)
+    w_run = 0.0 if m == -math.inf else math.exp(m - m_new)
+    w_blk = math.exp(m_b - m_new)
+    acc_new = None if acc_b is None else w_run * acc + w_blk * acc_b
+    return m_new, w_run * l + w_blk * l_b, acc_new
+
+
 def online_softmax_states(scores, block: int):
     """Running (m, l) after each block of a score row.
 
     "IO-Aware Attention: Tiling the Score Matrix Without Materializing It",
-    section "Softmax over blocks, exactly", the recurrence for m_i and l_i:
-    the new maximum is the max of the old one and the block's maximum; the old
-    sum is multiplied by exp(m_old - m_new) before the block's terms
-    exp(s_j - m_new) are added.  Start: m = -inf, l = 0.
+    section "Softmax over blocks, exactly": after each block the running
+    maximum is the larger of the previous one and the block's, and the
+    running sum is re-expressed relative to it, the part accumulated so far
+    scaled by exp(old max - new max).  Start: m = -inf, l = 0.  Here each
+    block is first summarised on its own maximum and then merged into the
+    running state (``_rescale_merge``), which gives the same (m, l).
 
     Returns a list of (m, l) pairs, one per block, in block order.
     """
     if block < 1:
         raise ValueError("block must be at least 1")
     s = _as_f64(scores).ravel()
-    m, l = -math.inf, 0.0
+    state = (-math.inf, 0.0, None)
     states = []
     for start in range(0, s.size, block):
-        sb = s[start:start + block]
-        m_new = max(m, float(sb.max()))
-        l = l * math.exp(m - m_new) + float(np.exp(sb - m_new).sum())
-        m = m_new
-        states.append((m, l))
+        state = _rescale_merge(state, _block_summary(s[start:start + block]))
+        states.append((state[0], state[1]))
     return states
 
 
@@ -162,30 +184,25 @@ def online_attention(q, K, V, block: int):
     """The blockwise online form for one query, never holding more than one
     block of scores.
 
-    "E8.1 IO-aware attention", "Do it in code" (block must be >= 1, otherwise
-    ValueError), with the recurrence of "IO-Aware Attention: Tiling the Score
-    Matrix Without Materializing It", section "Softmax over blocks, exactly":
-    per block, new_m = max(m, block max); rescale the running sum and the
-    running weighted value sum by exp(m - new_m); add the block's
-    exp(score - new_m) terms; divide once at the end.
+    "E8.1 IO-aware attention", "Do it in code": a function of one query, the
+    keys, the values and the block size (below 1 it raises ValueError) that
+    walks the keys block by block.  Each block's scores (scale 1/sqrt(d)) are
+    summarised on their own maximum, merged into the running (m, l, weighted
+    value sum) with the rescaling of "IO-Aware Attention", section "Softmax
+    over blocks, exactly", and the weighted sum is divided by l once, after
+    the last block.
     """
     if block < 1:
         raise ValueError("block must be at least 1")
     q = _as_f64(q)
     K = _as_f64(K)
     V = _as_f64(V)
-    n = K.shape[0]
     scale = 1.0 / math.sqrt(q.shape[0])
-    m, l = -math.inf, 0.0
-    acc = np.zeros(V.shape[1])
-    for start in range(0, n, block):
-        s = (K[start:start + block] @ q) * scale
-        m_new = max(m, float(s.max()))
-        r = math.exp(m - m_new)
-        e = np.exp(s - m_new)
-        l = l * r + float(e.sum())
-        acc = acc * r + e @ V[start:start + block]
-        m = m_new
+    state = (-math.inf, 0.0, np.zeros(V.shape[1]))
+    for start in range(0, K.shape[0], block):
+        scores = (K[start:start + block] @ q) * scale
+        state = _rescale_merge(state, _block_summary(scores, V[start:start + block]))
+    _, l, acc = state
     return acc / l
 
 

@@ -14,9 +14,9 @@ materialised:
     dQ = scale * dS K,   dK = scale * dS^T Q
 
 "IO-Aware Attention: Tiling the Score Matrix Without Materializing It",
-section "What has to stay in fast memory": the backward pass needs the softmax
-output, which is not stored, so it is recomputed from Q, K, V and the saved
-per-row normalisation constants.  ``attention_backward_from_lse`` follows that
+section "What has to stay in fast memory": the forward keeps only O and one
+normaliser per query row, so the probabilities the gradients use are rebuilt
+from Q, K, V and those per-row values.  ``attention_backward_from_lse`` follows that
 route (P = exp(S - lse), D from dO and O); ``attention_backward`` is the plain
 definition.  The derivative formulas themselves are not on the pages; they
 are the calculus of the forward definition and are pinned in

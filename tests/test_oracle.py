@@ -548,40 +548,42 @@ def test_combine_is_shift_invariant():
 _ATT = __import__("sys").modules["oracle.attention"]
 
 
-def _mut_states_no_rescale(scores, block):
-    s = np.asarray(scores, dtype=np.float64).ravel()
-    m, l, out = -math.inf, 0.0, []
-    for i in range(0, s.size, block):
-        sb = s[i:i + block]
-        m_new = max(m, float(sb.max()))
-        l = l + float(np.exp(sb - m_new).sum())          # old sum not rescaled
-        m = m_new
-        out.append((m, l))
-    return out
+def _states_with_merge(merge):
+    """online_softmax_states with its merge step replaced."""
+    def states(scores, block):
+        if block < 1:
+            raise ValueError("block must be at least 1")
+        s = np.asarray(scores, dtype=np.float64).ravel()
+        run, out = (-math.inf, 0.0), []
+        for i in range(0, s.size, block):
+            sb = s[i:i + block]
+            m_b = float(sb.max())
+            run = merge(run, (m_b, float(np.exp(sb - m_b).sum())))
+            out.append(run)
+        return out
+    return states
 
 
-def _mut_states_inverted_rescale(scores, block):
-    s = np.asarray(scores, dtype=np.float64).ravel()
-    m, l, out = -math.inf, 0.0, []
-    for i in range(0, s.size, block):
-        sb = s[i:i + block]
-        m_new = max(m, float(sb.max()))
-        l = (l * math.exp(m_new - m) if l else 0.0) + float(np.exp(sb - m_new).sum())
-        m = m_new
-        out.append((m, l))
-    return out
+def _merge_no_rescale(run, blk):
+    m_new = max(run[0], blk[0])
+    return m_new, run[1] + blk[1] * math.exp(blk[0] - m_new)       # old sum not rescaled
 
 
-def _mut_states_block_max_only(scores, block):
-    s = np.asarray(scores, dtype=np.float64).ravel()
-    m, l, out = -math.inf, 0.0, []
-    for i in range(0, s.size, block):
-        sb = s[i:i + block]
-        m_new = float(sb.max())                          # running max forgotten
-        l = l * math.exp(m - m_new) + float(np.exp(sb - m_new).sum())
-        m = m_new
-        out.append((m, l))
-    return out
+def _merge_inverted_rescale(run, blk):
+    m_new = max(run[0], blk[0])
+    w = math.exp(m_new - run[0]) if run[1] else 0.0                 # exponent upside down
+    return m_new, w * run[1] + blk[1] * math.exp(blk[0] - m_new)
+
+
+def _merge_block_max_only(run, blk):
+    m_new = blk[0]                                                  # running max forgotten
+    w = math.exp(run[0] - m_new) if run[1] else 0.0
+    return m_new, w * run[1] + blk[1]
+
+
+_mut_states_no_rescale = _states_with_merge(_merge_no_rescale)
+_mut_states_inverted_rescale = _states_with_merge(_merge_inverted_rescale)
+_mut_states_block_max_only = _states_with_merge(_merge_block_max_only)
 
 
 def _online_variant(rescale_acc=True, rescale_sum=True, scaled=True):
@@ -592,12 +594,14 @@ def _online_variant(rescale_acc=True, rescale_sum=True, scaled=True):
         scale = 1.0 / math.sqrt(q.shape[0]) if scaled else 1.0
         m, l, acc = -math.inf, 0.0, np.zeros(V.shape[1])
         for i in range(0, K.shape[0], block):
-            s = (K[i:i + block] @ q) * scale
-            m_new = max(m, float(s.max()))
-            r = math.exp(m - m_new)
-            e = np.exp(s - m_new)
-            l = (l * r if rescale_sum else l) + float(e.sum())
-            acc = (acc * r if rescale_acc else acc) + e @ V[i:i + block]
+            sb = (K[i:i + block] @ q) * scale
+            m_b = float(sb.max())
+            e = np.exp(sb - m_b)
+            m_new = max(m, m_b)
+            w_run = 0.0 if m == -math.inf else math.exp(m - m_new)
+            w_blk = math.exp(m_b - m_new)
+            l = (w_run * l if rescale_sum else l) + w_blk * float(e.sum())
+            acc = (w_run * acc if rescale_acc else acc) + w_blk * (e @ V[i:i + block])
             m = m_new
         return acc / l
     return online

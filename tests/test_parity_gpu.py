@@ -3,9 +3,12 @@
 Inputs are the seeded synthetic tensors of io_aware_exact_amd.inputs; the
 oracle sees exactly the values uploaded (bf16-rounded for bf16 cases).
 Tolerances: max-abs error on O <= 1e-5 for fp32 inputs and <= 2e-2 for bf16
-inputs; max-abs error on LSE <= 1e-3.  Small cases compare every output;
-the full-size workloads compare sampled rows the oracle computes one by one,
-in the same launch configuration the benchmark times.
+inputs; max-abs error on LSE <= 1e-3.  Small cases compare every output.
+The full-size prefill workloads compare every row of every head (mid-length,
+full and causal), every row of one head plus sampled rows of two more (long),
+or every row of four heads (head width 128), computed by the oracle in
+chunks of query rows, in the same launch configuration the benchmark times;
+the full-size decode workloads compare sampled heads.
 """
 
 import math
@@ -84,21 +87,80 @@ def _sampled_rows(T, n, rng):
     return np.array(sorted(set(r for r in edge + rnd if 0 <= r < T)))
 
 
-@pytest.mark.parametrize("name", ["mid", "mid_causal", "long", "mid_d128", "mid_d128_causal"])
-def test_prefill_full_size_sampled(name):
+def _compare_head(w, q, k, v, o, lse, b, h, rows_per_chunk=4096):
+    """Every row of head (b, h) against the oracle, in chunks of query rows
+    (the causal mask uses each row's absolute index, so chunks are exact)."""
+    og, lg = o[b, h].cpu(), lse[b, h].cpu()
+    qb, kb, vb = to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h])
+    eo = el = 0.0
+    for r0 in range(0, w.Tq, rows_per_chunk):
+        rows = np.arange(r0, min(w.Tq, r0 + rows_per_chunk))
+        o_ref, lse_ref = oracle.attention(qb, kb, vb, w.scale, w.causal, rows=rows)
+        eo = max(eo, float(np.abs(to_f64(og[r0:r0 + rows.size]) - o_ref).max()))
+        el = max(el, float(np.abs(to_f64(lg[r0:r0 + rows.size]) - lse_ref).max()))
+    assert np.isfinite(to_f64(og)).all()
+    return eo, el
+
+
+@pytest.mark.parametrize("name", ["mid", "mid_causal"])
+def test_prefill_mid_every_head(name):
+    """The mid-length prefill (2x16x4096, K x 3), full and causal: every row of
+    every head, element by element, in the launch the benchmark times."""
     w = WORKLOADS[name]
-    say(f"case {w} (sampled rows)")
+    say(f"case {w} (every head, every row)")
     q, k, v = make_qkv(w)
     o, lse, kern = run_gpu(w, q, k, v)
     say(f"  kernel {kern}")
+    worst_o = worst_l = 0.0
+    for b in range(w.B):
+        for h in range(w.H):
+            eo, el = _compare_head(w, q, k, v, o, lse, b, h)
+            worst_o, worst_l = max(worst_o, eo), max(worst_l, el)
+    say(f"  {w.B * w.H} heads x {w.Tq} rows: max|dO|={worst_o:.3e} (tol {TOL_O[w.dtype]}), max|dLSE|={worst_l:.3e}")
+    assert worst_o <= TOL_O[w.dtype] and worst_l <= TOL_LSE
+
+
+def test_prefill_long_full_head():
+    """The long causal prefill (1x12x16384): every row of one head (in chunks
+    of 2048 rows) and sampled rows of two more, element by element."""
+    w = WORKLOADS["long"]
+    say(f"case {w} (one full head, two sampled)")
+    q, k, v = make_qkv(w)
+    o, lse, kern = run_gpu(w, q, k, v)
+    say(f"  kernel {kern}")
+    eo, el = _compare_head(w, q, k, v, o, lse, 0, 7, rows_per_chunk=2048)
+    say(f"  head 7, all {w.Tq} rows: max|dO|={eo:.3e}, max|dLSE|={el:.3e}")
+    assert eo <= TOL_O[w.dtype] and el <= TOL_LSE
     rng = np.random.default_rng(1000 + w.seed)
-    heads = [(0, 0), (w.B - 1, w.H - 1), (w.B // 2, w.H // 3)]
-    for b, h in heads:
-        rows = _sampled_rows(w.Tq, 48, rng)
+    for b, h in [(0, 0), (0, w.H - 1)]:
+        rows = _sampled_rows(w.Tq, 256, rng)
         o_ref, lse_ref = oracle.attention(to_f64(q[b, h]), to_f64(k[b, h]), to_f64(v[b, h]), w.scale, w.causal,
                                           rows=rows)
-        compare(w, o[b, h][torch.from_numpy(rows).cuda()], lse[b, h][torch.from_numpy(rows).cuda()],
-                o_ref, lse_ref, what=f"[b={b},h={h}, {rows.size} rows]")
+        idx = torch.from_numpy(rows).cuda()
+        compare(w, o[b, h][idx], lse[b, h][idx], o_ref, lse_ref, what=f"[b={b},h={h}, {rows.size} rows]")
+
+
+def test_gpt2_shape_peaked_rows():
+    """GPT-2-shaped causal prefill with K rows scaled by 4 (scores with a
+    spread of 4 after scaling, so most rows are dominated by a few keys):
+    every head, every row.  The largest error term is then the rounding of
+    the dominant probability and of the output, each up to 2^-9 of |v|."""
+    w = WORKLOADS["gpt2"].with_(name="gpt2_peaked", seed=11, k_factor=4.0)
+    full_check(w)
+
+
+@pytest.mark.parametrize("name", ["mid_d128", "mid_d128_causal"])
+def test_prefill_d128_full_size(name):
+    """The mid-length prefill at head width 128: every row of four heads."""
+    w = WORKLOADS[name]
+    say(f"case {w} (four full heads)")
+    q, k, v = make_qkv(w)
+    o, lse, kern = run_gpu(w, q, k, v)
+    say(f"  kernel {kern}")
+    for b, h in [(0, 0), (w.B - 1, w.H - 1), (0, 9), (1, 4)]:
+        eo, el = _compare_head(w, q, k, v, o, lse, b, h)
+        say(f"  [b={b},h={h}] max|dO|={eo:.3e}, max|dLSE|={el:.3e}")
+        assert eo <= TOL_O[w.dtype] and el <= TOL_LSE
 
 
 def test_decode_full_size_sampled():
