@@ -109,6 +109,12 @@ __host__ __device__ __forceinline__ int tile_blocks(int qt, int bq, int bk, int 
     return (kend + bk - 1) / bk;
 }
 
+// Slices per head in the XCD-aware tile order: 8 / gcd(BH, 8).
+__host__ __device__ __forceinline__ int head_slices(int BH) {
+    const int g = (BH & 1) ? 1 : (BH & 2) ? 2 : (BH & 4) ? 4 : 8;
+    return 8 / g;
+}
+
 // Chunks a tile of nblk key blocks is split into when a work unit takes at
 // most `chunk` blocks (chunk <= 0: never split).
 __host__ __device__ __forceinline__ int tile_chunks(int nblk, int chunk) {
@@ -177,6 +183,30 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
         const int p = ((round & 1) && full) ? round * 32 + 31 - pos : k;
         rank = p / per;
         bh = (p % per) * 8 + xcd;
+        cc = 0;
+    } else if (KS == 1 && chunk <= 0 && (BH & 7) != 0 && nqt % head_slices(BH) == 0) {
+        // B*H not a multiple of 8: each head's tiles are split into
+        // s = 8 / gcd(B*H, 8) slices by rank mod s, and XCD x (block ids
+        // x, x+8, ...) owns the B*H/gcd consecutive slices starting at slice
+        // x*B*H/gcd -- fewer than two heads per XCD, so their K/V stays in
+        // its L2 -- taken heaviest rank first.
+        const int sl_per_head = head_slices(BH);
+        const int spx = BH * sl_per_head / 8;          // slices per XCD
+        const int xcd = id & 7, k = id >> 3;
+        const int grp = k / spx, i = k % spx;
+        const int first = xcd * spx;
+        int sl = first, seen = 0;
+        for (int p = 0; p < sl_per_head; ++p) {        // slices of parity p, in order
+            const int lo = first + ((p - first % sl_per_head) + sl_per_head) % sl_per_head;
+            const int cnt = lo < first + spx ? (first + spx - 1 - lo) / sl_per_head + 1 : 0;
+            if (i < seen + cnt) {
+                sl = lo + (i - seen) * sl_per_head;
+                break;
+            }
+            seen += cnt;
+        }
+        rank = grp * sl_per_head + sl % sl_per_head;
+        bh = sl / sl_per_head;
         cc = 0;
     } else {
         bh = id % BH;
