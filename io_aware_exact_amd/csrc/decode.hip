@@ -206,24 +206,31 @@ void decode_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     }
 }
 
-// One workgroup of D threads per (batch, query head): merge its P partial
-// records, online over groups of CG partitions whose loads are all in flight
-// together (the merge is latency-bound, not bandwidth-bound).
+// Merge of each (batch, query head)'s P partial records: M = max_p m_p,
+// w_p = 2^(m_p - M), O = sum_p w_p o_p / sum_p w_p l_p and
+// LSE = (M + log2 L) ln 2 -- the rescaling merge of "IO-Aware Attention",
+// section "Parallelism and the cost of the split".  The merge is bound by the
+// latency of reading the records, not by bytes, so NPG adjacent lanes share
+// each output element: lane g of the group takes partitions g, g + NPG, ...,
+// all its loads in flight together (in groups of CG), and the NPG running
+// states are combined by lane exchanges with the same rescaling.
 constexpr int CG = 8;
+constexpr int NPG = 4;
 
 template <int D>
-__global__ __launch_bounds__(D)
+__global__ __launch_bounds__(D * NPG)
 void decode_combine_kernel(const float* __restrict__ part, uint16_t* __restrict__ O,
                            float* __restrict__ LSE, int P) {
     const int bh = blockIdx.x;
-    const int d = threadIdx.x;
+    const int g = threadIdx.x % NPG;
+    const int d = threadIdx.x / NPG;
     const float* rec = part + (size_t)bh * P * (D + 2);
     float M = kNegInf, L = 0.f, acc = 0.f;
-    for (int p0 = 0; p0 < P; p0 += CG) {
+    for (int p0 = g; p0 < P; p0 += NPG * CG) {
         float mk[CG], lk[CG], ok[CG];
 #pragma unroll
         for (int i = 0; i < CG; ++i) {
-            const int p = min(p0 + i, P - 1);   // repeats of the last record get weight 0 below
+            const int p = min(p0 + NPG * i, P - 1);   // past the last record: weight 0 below
             const float* r = rec + (size_t)p * (D + 2);
             mk[i] = r[D];
             lk[i] = r[D + 1];
@@ -232,21 +239,34 @@ void decode_combine_kernel(const float* __restrict__ part, uint16_t* __restrict_
         float mg = M;
 #pragma unroll
         for (int i = 0; i < CG; ++i)
-            if (p0 + i < P) mg = fmaxf(mg, mk[i]);
+            if (p0 + NPG * i < P) mg = fmaxf(mg, mk[i]);
         const float mu = (mg == kNegInf) ? 0.f : mg;
         const float alpha = fast_exp2(M - mu);
         L *= alpha;
         acc *= alpha;
 #pragma unroll
         for (int i = 0; i < CG; ++i) {
-            const float w = (p0 + i < P) ? fast_exp2(mk[i] - mu) : 0.f;
+            const float w = (p0 + NPG * i < P) ? fast_exp2(mk[i] - mu) : 0.f;
             L = __builtin_fmaf(w, lk[i], L);
             acc = __builtin_fmaf(w, ok[i], acc);
         }
         M = mg;
     }
-    O[(size_t)bh * D + d] = (uint16_t)(pack_bf16x2(acc / L, 0.f) & 0xffffu);
-    if (d == 0 && LSE != nullptr) LSE[bh] = (M + __builtin_log2f(L)) * 0.69314718055994530942f;
+    // the NPG lanes of the element (a lane without partitions has M = -inf, L = acc = 0)
+#pragma unroll
+    for (int x = 1; x < NPG; x <<= 1) {
+        const float Mo = __shfl_xor(M, x), Lo = __shfl_xor(L, x), ao = __shfl_xor(acc, x);
+        const float mm = fmaxf(M, Mo);
+        const float mu = (mm == kNegInf) ? 0.f : mm;
+        const float wa = fast_exp2(M - mu), wb = fast_exp2(Mo - mu);
+        L = wa * L + wb * Lo;
+        acc = wa * acc + wb * ao;
+        M = mm;
+    }
+    if (g == 0) {
+        O[(size_t)bh * D + d] = (uint16_t)(pack_bf16x2(acc / L, 0.f) & 0xffffu);
+        if (d == 0 && LSE != nullptr) LSE[bh] = (M + __builtin_log2f(L)) * 0.69314718055994530942f;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -510,7 +530,7 @@ hipError_t launch_dg(const DecodeArgs& a, hipStream_t stream, const char** name)
                        static_cast<uint16_t*>(a.o), a.lse, a.Hkv, G, a.Tkv, a.num_splits, a.c, direct ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && !direct) {
-        hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.H), dim3(D), 0, stream,
+        hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.H), dim3(D * NPG), 0, stream,
                            static_cast<const float*>(a.workspace), static_cast<uint16_t*>(a.o), a.lse,
                            a.num_splits);
         e = hipGetLastError();
@@ -536,7 +556,7 @@ hipError_t launch_mfma(const DecodeArgs& a, hipStream_t stream, const char** nam
                        static_cast<uint16_t*>(a.o), a.lse, a.Hkv, G, a.Tkv, a.num_splits, a.c, direct ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && !direct) {
-        hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.H), dim3(D), 0, stream,
+        hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.H), dim3(D * NPG), 0, stream,
                            static_cast<const float*>(a.workspace), static_cast<uint16_t*>(a.o), a.lse,
                            a.num_splits);
         e = hipGetLastError();
