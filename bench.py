@@ -691,7 +691,81 @@ def achievable_ceilings(torch):
         out["mfma_loop_TFLOPs"] = rate
         out["mfma_loop"] = ("matrix-pipe probe (libattn_probe.so): 2048 workgroups of 4 waves, each wave 4 "
                             "independent chains of v_mfma_f32_32x32x16_bf16 from registers, 4096 steps")
+    rates = instruction_rates(torch)
+    if rates is not None:
+        out["issue"] = rates
     return out
+
+
+ISSUE_MODES = ("exp2_mul", "fma_mul", "mfma", "mfma_beside_exp2", "mfma_beside_fma", "prefill_block_mix")
+ISSUE_OPS = {"exp2_mul": 16, "fma_mul": 16, "mfma": 2}   # independent ops per loop iteration
+
+
+def instruction_rates(torch, waves=(1, 2, 3), rounds: int = 8):
+    """Issue and pipe rates from the instruction-mix probe of libattn_probe.so.
+    For each mode and each count w of waves per SIMD (held there by an LDS
+    reservation; `rounds` full rounds of CUs * w workgroups of 4 waves): the
+    shader-clock cycles one SIMD spends per loop iteration of one wave (the
+    event-timed launch over the wave-iterations each SIMD ran, times the clock
+    the waves' s_memtime / s_memrealtime ratio shows), and that clock.  Derived
+    at 3 waves per SIMD (the prefill kernels' occupancy): cycles per exp2+mul
+    pair, per fma+mul pair, per 32x32x16 bf16 MFMA, and the share of the
+    prefill's per-block mix (16 MFMAs and the softmax of 32 scores per lane,
+    from registers) that the matrix pipe is busy.  None if the probe library
+    is not built."""
+    import ctypes
+
+    path = os.path.join(ROOT, "io_aware_exact_amd", "libattn_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    if not hasattr(lib, "probe_issue"):
+        return None
+    lib.probe_issue.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.probe_issue.restype = ctypes.c_int
+    threads = lib.probe_issue_threads()
+    wpb = threads // 64
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    ops = torch.full((lib.probe_issue_operand_bytes() // 2,), 0.0625, dtype=torch.bfloat16, device="cuda")
+    blocks_max = cus * max(waves) * rounds
+    out = torch.empty(blocks_max * threads, dtype=torch.float32, device="cuda")
+    ticks = torch.empty(blocks_max * wpb * 2, dtype=torch.int64, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    cycles, clock_mhz = {}, {}
+    for mode, name in enumerate(ISSUE_MODES):
+        iters = 256 if name == "prefill_block_mix" else 1024
+        cycles[name], clock_mhz[name] = {}, {}
+        for w in waves:
+            blocks = cus * w * rounds
+
+            def call():
+                rc = lib.probe_issue(mode, w, blocks, iters, ctypes.c_void_p(ops.data_ptr()),
+                                     ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ticks.data_ptr()), stream)
+                if rc != 0:
+                    raise RuntimeError(f"issue probe launch failed (hipError {rc})")
+
+            ms = time_steps(torch, call, 3, 1)
+            t = ticks[: blocks * wpb * 2].view(-1, 2).double().sum(0)
+            mhz = 100.0 * t[0].item() / t[1].item()
+            wave_iters_per_simd = blocks * wpb * iters / (4 * cus)
+            cycles[name][str(w)] = ms * 1e-3 / wave_iters_per_simd * mhz * 1e6
+            clock_mhz[name][str(w)] = mhz
+    del ops, out, ticks
+    w3 = str(max(waves))
+    mfma = cycles["mfma"][w3] / ISSUE_OPS["mfma"]
+    return {
+        "simd_cycles_per_iteration": cycles,
+        "clock_mhz": clock_mhz,
+        "waves_per_simd": list(waves),
+        "rounds": rounds,
+        "cycles_per_exp2_mul": cycles["exp2_mul"][w3] / ISSUE_OPS["exp2_mul"],
+        "cycles_per_fma_mul": cycles["fma_mul"][w3] / ISSUE_OPS["fma_mul"],
+        "cycles_per_mfma_32x32x16_bf16": mfma,
+        "prefill_block_mix_mfma_share": 16 * mfma / cycles["prefill_block_mix"][w3],
+        "probe": ("instruction-mix probe (libattn_probe.so, issue_probe.hip): loops with no memory traffic, "
+                  "w waves per SIMD held by an LDS reservation; modes " + ", ".join(ISSUE_MODES)),
+    }
 
 
 def mfma_loop_rate(torch, blocks: int = 2048, iters: int = 4096):
@@ -887,6 +961,11 @@ def main():
         result["achievable"] = ceil
         log(f"[bench] achievable: copy {ceil['copy_GBps']:.0f} GB/s, bf16 GEMM {ceil['bf16_gemm_TFLOPs']:.0f} TFLOP/s,"
             f" MFMA loop {ceil.get('mfma_loop_TFLOPs', float('nan')):.0f} TFLOP/s")
+        if "issue" in ceil:
+            iss = ceil["issue"]
+            log(f"[bench] issue probe (3 waves/SIMD): exp2+mul {iss['cycles_per_exp2_mul']:.2f}, fma+mul "
+                f"{iss['cycles_per_fma_mul']:.2f}, MFMA {iss['cycles_per_mfma_32x32x16_bf16']:.1f} cycles; "
+                f"prefill block mix keeps the matrix pipe {100 * iss['prefill_block_mix_mfma_share']:.0f}% busy")
     if args.copy_calibration:
         result["copy_calibration_bytes"] = copy_calibration(torch)
     result["kernel_sources_digest"] = kernel_sources_digest()

@@ -3,8 +3,8 @@
     python -m io_aware_exact_amd.build          # compile every source for gfx950 and link
 
 Also builds io_aware_exact_amd/libattn_probe.so from probe/: a matrix-pipe
-throughput probe the benchmark times beside the attention kernels (not part of
-the attention library or its C ABI).
+throughput probe and an instruction-mix probe that the benchmark times beside
+the attention kernels (not part of the attention library or its C ABI).
 
 Every .hip source is compiled for gfx950 only; the C ABI (api.cpp) is host
 C++.  Packed fp32 VALU instructions are disabled in device code.

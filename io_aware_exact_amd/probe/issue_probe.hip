@@ -1,0 +1,184 @@
+// Instruction-mix probes for gfx950 (measurement aids for the benchmark, not
+// part of the attention library).  Each kernel runs a loop with no memory
+// traffic, so only issue, the VALU, the transcendental unit and the matrix
+// pipe bound it.  Each workgroup of 4 waves reserves a share of the 160 KiB
+// of LDS per compute unit that lets exactly w workgroups reside on one unit,
+// so every SIMD holds w waves at a time however small the register use; the
+// grid is many such rounds.  Every wave records the s_memtime (shader clock)
+// and s_memrealtime (100 MHz) ticks its loop took, so the host reads the
+// clock the loop ran at from their ratio.
+//
+// Modes (per loop iteration, 16 independent chains where it applies):
+//   0  16 x (v_exp_f32 then v_mul_f32)          transcendental rate
+//   1  16 x (v_fma_f32 then v_mul_f32)          plain VALU rate
+//   2  2 x v_mfma_f32_32x32x16_bf16             matrix-pipe rate
+//   3  mode 0 interleaved with 2 MFMAs           MFMA beside exp
+//   4  mode 1 interleaved with 2 MFMAs           MFMA beside plain VALU
+//   5  one key block of the head-width-64 prefill for 32 query rows, from
+//      registers: 8 QK MFMAs, the softmax of 32 scores per lane (FMA, exp2,
+//      row-sum adds, bf16 packs) and 8 PV MFMAs, with the kernel's data
+//      dependences (the loop-carried accumulators and reference)
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+// Every instantiation is compiled for 3 waves per SIMD, so the code is the
+// same whatever occupancy the LDS reservation allows; the compiler's note that
+// one or two waves per SIMD miss that target is expected.
+#pragma clang diagnostic ignored "-Wpass-failed"
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    f32x2_t f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+// LDS each workgroup reserves so that W (1..3) workgroups fit on a compute
+// unit of 160 KiB and one more does not.
+constexpr int reserve_floats(int W) { return (W == 1 ? 96 : W == 2 ? 64 : 48) * 256; }
+
+template <int MODE, int W>
+__global__ __launch_bounds__(kThreads, 3)
+void issue_probe_kernel(int iters, const u32x4_t* __restrict__ operands, float* __restrict__ out,
+                        long long* __restrict__ ticks) {
+    __shared__ float reserve[reserve_floats(W)];   // occupancy limiter only
+    const int tid = threadIdx.x;
+    if (iters < 0) {                     // never taken: keeps the reservation
+        reserve[tid] = 0.f;
+        __syncthreads();
+        out[tid] = reserve[(tid + 1) % kThreads];
+        return;
+    }
+    // 20 bf16x8 operands per lane (finite values from the caller)
+    bf16x8_t q[4], k[8], v[8];
+    const u32x4_t* src = operands + (tid & 63);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) q[t] = __builtin_bit_cast(bf16x8_t, src[64 * t]);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) k[t] = __builtin_bit_cast(bf16x8_t, src[64 * (4 + t)]);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[t] = __builtin_bit_cast(bf16x8_t, src[64 * (12 + t)]);
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = -1e-3f * (float)(tid + i);
+    f32x16_t c0 = {}, c1 = {};
+    float m = 0.5f, l = 0.f;
+    const float c = 0.18f;
+    const long long r0 = __builtin_amdgcn_s_memrealtime();
+    const long long t0 = __builtin_amdgcn_s_memtime();
+    for (int it = 0; it < iters; ++it) {
+        if constexpr (MODE == 0 || MODE == 3) {
+            if constexpr (MODE == 3) c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[0], q[0], c0, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = __builtin_amdgcn_exp2f(x[i]) * -0.5f;
+            if constexpr (MODE == 3) c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[1], q[1], c1, 0, 0, 0);
+#pragma unroll
+            for (int i = 8; i < 16; ++i) x[i] = __builtin_amdgcn_exp2f(x[i]) * -0.5f;
+        } else if constexpr (MODE == 1 || MODE == 4) {
+            if constexpr (MODE == 4) c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[0], q[0], c0, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = __builtin_fmaf(x[i], -0.5f, 0.25f) * -0.5f;
+            if constexpr (MODE == 4) c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[1], q[1], c1, 0, 0, 0);
+#pragma unroll
+            for (int i = 8; i < 16; ++i) x[i] = __builtin_fmaf(x[i], -0.5f, 0.25f) * -0.5f;
+        } else if constexpr (MODE == 2) {
+            c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[0], q[0], c0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[1], q[1], c1, 0, 0, 0);
+        } else {
+            asm volatile("" : "+v"(k[0]), "+v"(k[4]));   // opaque every iteration: nothing is hoisted
+            f32x16_t s0 = {}, s1 = {};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[t], q[t], s0, 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[4 + t], q[t], s1, 0, 0, 0);
+            float sv[32];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                sv[r] = s0[r];
+                sv[16 + r] = s1[r];
+            }
+            uint32_t pw[16];
+            float rs = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i], c, -m));
+                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i + 1], c, -m));
+                pw[i] = pack2(p0, p1);
+                rs += p0 + p1;
+            }
+            l += rs;
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const u32x4_t pv = {pw[4 * st], pw[4 * st + 1], pw[4 * st + 2], pw[4 * st + 3]};
+                const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pv);
+                c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[2 * st], pb, c0, 0, 0, 0);
+                c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[2 * st + 1], pb, c1, 0, 0, 0);
+            }
+            m += 1e-7f * l;    // loop-carried: the next block's reference depends on this one
+        }
+    }
+    const long long t1 = __builtin_amdgcn_s_memtime();
+    const long long r1 = __builtin_amdgcn_s_memrealtime();
+    float sum = l + m;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += x[i] + c0[i] + c1[i];
+    out[(size_t)blockIdx.x * kThreads + tid] = sum;
+    if ((tid & 63) == 0) {
+        const size_t w = (size_t)blockIdx.x * (kThreads / 64) + (tid >> 6);
+        ticks[2 * w] = t1 - t0;
+        ticks[2 * w + 1] = r1 - r0;
+    }
+}
+
+template <int MODE>
+static hipError_t launch_mode(int waves, int blocks, int iters, const u32x4_t* ops, float* out, long long* ticks,
+                              hipStream_t stream) {
+    if (waves == 1)
+        hipLaunchKernelGGL((issue_probe_kernel<MODE, 1>), dim3(blocks), dim3(kThreads), 0, stream, iters, ops, out, ticks);
+    else if (waves == 2)
+        hipLaunchKernelGGL((issue_probe_kernel<MODE, 2>), dim3(blocks), dim3(kThreads), 0, stream, iters, ops, out, ticks);
+    else
+        hipLaunchKernelGGL((issue_probe_kernel<MODE, 3>), dim3(blocks), dim3(kThreads), 0, stream, iters, ops, out, ticks);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+// Number of modes, and the bf16x8 operand words the caller provides
+// (20 per lane of a wave: 20 * 64 * 16 bytes).
+int probe_issue_modes(void) { return 6; }
+int probe_issue_operand_bytes(void) { return 20 * 64 * 16; }
+int probe_issue_threads(void) { return kThreads; }
+
+// Enqueue one launch of mode `mode` on `stream` at `waves` (1..3) waves per
+// SIMD: `blocks` workgroups of 256 threads (a multiple of the compute units
+// times `waves` fills whole rounds), `iters` loop iterations each; `out`
+// holds blocks * 256 floats and `ticks` blocks * 8 long longs (per wave: the
+// s_memtime ticks, then the s_memrealtime ticks of its loop).  Returns the
+// hipError_t of the launch; invalid arguments are refused before any launch.
+int probe_issue(int mode, int waves, int blocks, int iters, const void* operands, float* out, long long* ticks,
+                hipStream_t stream) {
+    if (mode < 0 || mode > 5 || waves < 1 || waves > 3 || blocks < 1 || iters < 1 || !operands || !out || !ticks)
+        return (int)hipErrorInvalidValue;
+    const u32x4_t* ops = static_cast<const u32x4_t*>(operands);
+    switch (mode) {
+        case 0: return (int)launch_mode<0>(waves, blocks, iters, ops, out, ticks, stream);
+        case 1: return (int)launch_mode<1>(waves, blocks, iters, ops, out, ticks, stream);
+        case 2: return (int)launch_mode<2>(waves, blocks, iters, ops, out, ticks, stream);
+        case 3: return (int)launch_mode<3>(waves, blocks, iters, ops, out, ticks, stream);
+        case 4: return (int)launch_mode<4>(waves, blocks, iters, ops, out, ticks, stream);
+        default: return (int)launch_mode<5>(waves, blocks, iters, ops, out, ticks, stream);
+    }
+}
+
+}  // extern "C"

@@ -148,6 +148,28 @@ def test_mfma_probe_library_exports():
     assert lib.probe_mfma_loop(1, 1, None, None) != 0
 
 
+def test_issue_probe_library_exports():
+    import ctypes
+
+    path = os.path.join(ROOT, "io_aware_exact_amd", "libattn_probe.so")
+    if not os.path.exists(path):
+        pytest.skip("probe library not built")
+    lib = ctypes.CDLL(path)
+    lib.probe_issue.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    bench = load_bench()
+    assert lib.probe_issue_modes() == len(bench.ISSUE_MODES)
+    assert lib.probe_issue_threads() == 256
+    assert lib.probe_issue_operand_bytes() == 20 * 64 * 16     # 20 bf16x8 operands per lane
+    # rejected before any launch: bad mode, occupancy outside 1..3, empty grid, null pointers
+    one = ctypes.c_void_p(1)
+    assert lib.probe_issue(6, 3, 1, 1, one, one, one, None) != 0
+    assert lib.probe_issue(0, 4, 1, 1, one, one, one, None) != 0
+    assert lib.probe_issue(0, 0, 1, 1, one, one, one, None) != 0
+    assert lib.probe_issue(0, 3, 0, 1, one, one, one, None) != 0
+    assert lib.probe_issue(0, 3, 1, 1, None, one, one, None) != 0
+
+
 ROCMINFO_SAMPLE = """
 *******
 Agent 1
