@@ -50,7 +50,8 @@
 //   and a wave whose rows all lie above a block skips its math for that block.
 // * Tiles are launched heaviest-first (last query tiles first) and the
 //   linear block id keeps every tile of one (batch, head) on one XCD when the
-//   number of heads is a multiple of 8.
+//   number of heads is a multiple of 8 (full attention: an XCD's heads one
+//   after another), else a head's tiles on as few XCDs as the count allows.
 // * Grids of too few 128-row tiles (d = 64) use 64-row tiles whose key loop
 //   is split over the two waves of a pair and merged through LDS at the end
 //   (KS = 2 below), which halves the serial chain of the heaviest tiles.
@@ -183,6 +184,16 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
         const int p = ((round & 1) && full) ? round * 32 + 31 - pos : k;
         rank = p / per;
         bh = (p % per) * 8 + xcd;
+        cc = 0;
+    } else if (!CAUSAL && KS == 1 && chunk <= 0 && (BH & 7) == 0) {
+        // Full attention, B*H a multiple of 8: XCD x (block ids x, x+8, ...)
+        // runs its heads x, x+8, ... one after another, every tile of a head
+        // before the next head, so the few heads it streams at once keep
+        // their K/V in its L2 (tiles of a head cost the same: no order by
+        // weight is needed).
+        const int xcd = id & 7, k = id >> 3;
+        rank = k % nqt;
+        bh = (k / nqt) * 8 + xcd;
         cc = 0;
     } else if (KS == 1 && chunk <= 0 && (BH & 7) != 0 && nqt % head_slices(BH) == 0) {
         // B*H not a multiple of 8: each head's tiles are split into
