@@ -201,6 +201,8 @@ PREFILL_CASES = [
     (1, 1, 300, 17, False),     # fewer keys than a block
     (1, 1, 33, 700, True),
     (3, 1, 1000, 1000, True),
+    (2, 4, 300, 300, False),    # B*H a multiple of 8, full: heads run one after another per XCD
+    (1, 16, 257, 513, False),   # ... with Tq < Tkv and ragged ends
 ]
 
 
