@@ -258,8 +258,9 @@ size_t attn_bwd_workspace_bytes(int B, int H, int Tq);
  *   workspace  at least attn_bwd_workspace_bytes(B,H,Tq) bytes; contents on
  *              entry are ignored
  *
- * Three kernels on `stream` (row statistics, dK/dV per key tile, dQ per query
- * tile); no atomics, so results are deterministic.  Products are bf16 MFMA with
+ * Two kernels on `stream`: dQ per query tile, which also writes each row's
+ * statistics (lse * log2 e and D = sum dO * O) to the workspace, then dK/dV per
+ * key tile, which reads them; no atomics, so results are deterministic.  Products are bf16 MFMA with
  * fp32 accumulation; P and dS are rounded to bf16 as MFMA operands.
  * Errors: as attn_fwd, plus ATTN_EINVAL for NULL dout/lse/dq/dk/dv or
  * overlapping buffers, ATTN_EWORKSPACE for a missing or small workspace.

@@ -12,8 +12,12 @@
 //   dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D)
 //   dQ = scale * dS K,   dK = scale * dS^T Q
 //
-// Three kernels, no atomics:
-// * bwd_stats: per query row (lse2, D) -- one streaming pass over O and dO.
+// Two kernels, no atomics, dQ first:
+// * bwd_dq: one workgroup per 128-query tile, the forward's layout (one query
+//   per lane, key blocks of 64 at d = 64, 32 at d = 128): S^T = K Q^T,
+//   dP^T = V dO^T, dQ^T += K^T dS^T with K^T read transposed from the ring.
+//   It first forms its rows' (lse2, D) from LSE, O and the dO fragment it
+//   holds anyway, and writes them for bwd_dkdv.
 // * bwd_dkdv: one workgroup per 128-key tile (32 keys per wave, one key per
 //   lane column).  K and V of the wave stay in VGPRs as MFMA B operands; Q and
 //   dO blocks (64 rows at d = 64, 32 at d = 128) and their row statistics
@@ -21,9 +25,6 @@
 //   as rows), then dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T read by
 //   ds_read_b64_tr_b16, so P and dS go from the accumulator layout to the B
 //   operand with only a bf16 pack.
-// * bwd_dq: one workgroup per 128-query tile, the forward's layout (one query
-//   per lane, key blocks of 64 at d = 64, 32 at d = 128): S^T = K Q^T,
-//   dP^T = V dO^T, dQ^T += K^T dS^T with K^T read transposed from the ring.
 // Q and dO (in bwd_dkdv) and K (in bwd_dq) are read both as rows and
 // transposed, so their LDS chunk swizzle is conflict-free for both patterns.
 // Products are bf16 MFMA with fp32 accumulation; P and dS are rounded to
@@ -98,30 +99,6 @@ __device__ __forceinline__ void tr_offsets(int lane, uint32_t (&o)[D / 32][2]) {
         o[dt][0] = tr_off<D>(row, col);
         o[dt][1] = tr_off<D>(row + 8, col);
     }
-}
-
-// ---------------------------------------------------------------- statistics
-
-// stats[bh * Tq + i] = (lse_i * log2 e, sum_d dO_id O_id); D/8 lanes per row.
-template <int D>
-__global__ __launch_bounds__(256)
-void bwd_stats_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
-                      const float* __restrict__ LSE, float2* __restrict__ stats, long long rows) {
-    constexpr int LPR = D / 8;
-    const long long r = (long long)blockIdx.x * (256 / LPR) + (threadIdx.x / LPR);
-    const int part = threadIdx.x % LPR;
-    float acc = 0.f;
-    if (r < rows) {
-        const u32x4_t o = *reinterpret_cast<const u32x4_t*>(O + r * D + 8 * part);
-        const u32x4_t g = *reinterpret_cast<const u32x4_t*>(dO + r * D + 8 * part);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc = __builtin_fmaf(bf16_lo(o[i]), bf16_lo(g[i]), acc);
-            acc = __builtin_fmaf(bf16_hi(o[i]), bf16_hi(g[i]), acc);
-        }
-    }
-    acc = group_sum<LPR>(acc);
-    if (r < rows && part == 0) stats[r] = make_float2(LSE[r] * 1.44269504088896340736f, acc);
 }
 
 // ------------------------------------------------------------------ dK, dV
@@ -406,7 +383,8 @@ template <int D, bool CAUSAL, int KS = 1>
 __global__ __launch_bounds__(DQ_WAVES * 64, 2)
 void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                   const float2* __restrict__ stats, float* __restrict__ dQ,
+                   const uint16_t* __restrict__ O, const float* __restrict__ LSE,
+                   float2* __restrict__ stats, float* __restrict__ dQ,
                    int Tq, int Tkv, int BH, int nqt, float c, float scale) {
     using G = BwdGeo<D>;
     constexpr int ROWB = D * 2;
@@ -450,14 +428,21 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     if (qrow < Tq) {
         const u32x4_t* qs = reinterpret_cast<const u32x4_t*>(Q + qbase + (size_t)qrow * D + 8 * hf);
         const u32x4_t* gs = reinterpret_cast<const u32x4_t*>(dO + qbase + (size_t)qrow * D + 8 * hf);
+        const u32x4_t* os = reinterpret_cast<const u32x4_t*>(O + qbase + (size_t)qrow * D + 8 * hf);
 #pragma unroll
         for (int t = 0; t < TQ; ++t) {
             qf[t] = __builtin_bit_cast(bf16x8_t, qs[2 * t]);
-            gf[t] = __builtin_bit_cast(bf16x8_t, gs[2 * t]);
+            const u32x4_t g = gs[2 * t];
+            const u32x4_t o = os[2 * t];
+            gf[t] = __builtin_bit_cast(bf16x8_t, g);
+            // this lane's half of D = sum_d dO_d O_d (the other half is in lane ^ 32)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                dd = __builtin_fmaf(bf16_lo(o[i]), bf16_lo(g[i]), dd);
+                dd = __builtin_fmaf(bf16_hi(o[i]), bf16_hi(g[i]), dd);
+            }
         }
-        const float2 sv = stats[(size_t)bh * Tq + qrow];
-        lse2 = sv.x;
-        dd = sv.y;
+        lse2 = LSE[(size_t)bh * Tq + qrow] * 1.44269504088896340736f;
     } else {
 #pragma unroll
         for (int t = 0; t < TQ; ++t) {
@@ -465,6 +450,9 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
             gf[t] = qf[t];
         }
     }
+    dd = half_swap_sum(dd);
+    // the row statistics bwd_dkdv reads: one lane per row writes them
+    if (qrow < Tq && hf == 0 && kh == 0) stats[(size_t)bh * Tq + qrow] = make_float2(lse2, dd);
 
     const int kend = CAUSAL ? min(Tkv, q0 + BQT + off) : Tkv;
     const int nblk = (kend + BK - 1) / BK;
@@ -633,18 +621,33 @@ bool bwd_q_halves(const BackwardArgs& a) {
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_c(const BackwardArgs& a, hipStream_t stream) {
     const int BHn = a.B * a.H;
-    const long long rows = (long long)BHn * a.Tq;
     float2* stats = static_cast<float2*>(a.workspace);
-    constexpr int RPW = 256 / (D / 8);
-    hipLaunchKernelGGL((bwd_stats_kernel<D>), dim3((unsigned)((rows + RPW - 1) / RPW)), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout), a.lse, stats, rows);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     bool kv_halves = false, q_halves = false;
     if constexpr (D == 64) {
         kv_halves = bwd_kv_halves(a);
         q_halves = bwd_q_halves(a);
     }
+    // dQ first: it writes the row statistics that dK/dV reads
+    if constexpr (D == 64) {
+        if (q_halves) {
+            const int nqt = (a.Tq + BQ / 2 - 1) / (BQ / 2);
+            hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, 2>), dim3((unsigned)(nqt * BHn)), dim3(DQ_WAVES * 64), 0,
+                               stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                               static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout),
+                               static_cast<const uint16_t*>(a.o), a.lse, stats, a.dq, a.Tq, a.Tkv, BHn, nqt, a.c,
+                               a.scale);
+        }
+    }
+    if (!q_halves) {
+        const int nqt = (a.Tq + BQ - 1) / BQ;
+        hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(nqt * BHn)), dim3(DQ_WAVES * 64), 0, stream,
+                           static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                           static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout),
+                           static_cast<const uint16_t*>(a.o), a.lse, stats, a.dq, a.Tq, a.Tkv, BHn, nqt, a.c,
+                           a.scale);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     if constexpr (D == 64) {
         if (kv_halves) {
             const int nkt = (a.Tkv + BKV / 2 - 1) / (BKV / 2);
@@ -661,23 +664,6 @@ hipError_t launch_bwd_c(const BackwardArgs& a, hipStream_t stream) {
                            static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), stats, a.dk,
                            a.dv, a.Tq, a.Tkv, BHn, a.c, a.scale);
     }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if constexpr (D == 64) {
-        if (q_halves) {
-            const int nqt = (a.Tq + BQ / 2 - 1) / (BQ / 2);
-            hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, 2>), dim3((unsigned)(nqt * BHn)), dim3(DQ_WAVES * 64), 0,
-                               stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                               static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), stats, a.dq,
-                               a.Tq, a.Tkv, BHn, nqt, a.c, a.scale);
-        }
-    }
-    if (!q_halves) {
-        const int nqt = (a.Tq + BQ - 1) / BQ;
-        hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(nqt * BHn)), dim3(DQ_WAVES * 64), 0, stream,
-                           static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                           static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), stats, a.dq,
-                           a.Tq, a.Tkv, BHn, nqt, a.c, a.scale);
-    }
     return hipGetLastError();
 }
 
@@ -693,9 +679,9 @@ hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream, const
     const int bq2 = a.d == 128 ? BwdGeo<128>::BQ2 : BwdGeo<64>::BQ2;
     const int bk = a.d == 128 ? BwdGeo<128>::BK : BwdGeo<64>::BK;
     const bool kvh = bwd_kv_halves(a), qh = bwd_q_halves(a);
-    snprintf(g_name, sizeof g_name, "bwd_bf16_d%d<stats+dkdv(bk=%d,bq=%d%s)+dq(bq=%d,bk=%d%s)%s>", a.d,
-             kvh ? BKV / 2 : BKV, bq2, kvh ? ",query_halves=2" : "", qh ? BQ / 2 : BQ, bk,
-             qh ? ",key_halves=2" : "", a.causal ? ",causal" : "");
+    snprintf(g_name, sizeof g_name, "bwd_bf16_d%d<dq+stats(bq=%d,bk=%d%s)+dkdv(bk=%d,bq=%d%s)%s>", a.d,
+             qh ? BQ / 2 : BQ, bk, qh ? ",key_halves=2" : "", kvh ? BKV / 2 : BKV, bq2,
+             kvh ? ",query_halves=2" : "", a.causal ? ",causal" : "");
     *name = g_name;
     if (a.d == 128) {
         if (a.causal) return launch_bwd_c<128, true>(a, stream);
