@@ -146,7 +146,7 @@ size_t attn_decode_workspace_bytes(int B, int H, int d, int num_splits);
 
 /*
  * attn_decode_splits -- the number of key partitions the library picks for a
- * decode step (num_splits = 0): enough for about 512 workgroups (at most 32
+ * decode step (num_splits = 0): enough for about 512 workgroups (at most 16
  * partitions; 64 for groups of 4 or more query heads, whose kernel runs one
  * wave per workgroup), and none holding less than 64 KiB of K and V
  * (16384/d keys).  A single sequence offers only H

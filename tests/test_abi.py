@@ -219,9 +219,10 @@ def test_split_forward_workspace_formula():
 
 
 def test_decode_automatic_splits():
-    # 12 heads of one sequence: 512 workgroups would need 43 partitions; capped at 32,
-    # then halved until partitions hold >= 64 KiB of K+V (256 keys at d=64, 128 at d=128)
-    assert attn.attn_decode_splits(1, 12, 12, 16384, 64) == 32
+    # 12 heads of one sequence: 512 workgroups would need 43 partitions; capped at 16
+    # (8-wave workgroups), then halved until partitions hold >= 64 KiB of K+V (256 keys
+    # at d=64, 128 at d=128)
+    assert attn.attn_decode_splits(1, 12, 12, 16384, 64) == 16
     assert attn.attn_decode_splits(1, 12, 12, 4096, 64) == 16
     assert attn.attn_decode_splits(1, 12, 12, 1024, 64) == 4
     assert attn.attn_decode_splits(1, 12, 12, 300, 64) == 1
@@ -229,7 +230,7 @@ def test_decode_automatic_splits():
     assert attn.attn_decode_splits(16, 12, 12, 16384, 64) == 4    # 192 workgroups -> x4
     assert attn.attn_decode_splits(64, 32, 32, 8192, 128) == 1    # 2048 workgroups already
     # grouped-query: workgroups count kv heads x head tiles
-    assert attn.attn_decode_splits(64, 32, 16, 8192, 128) == 1     # groups of 2: VALU kernel, 4-wave groups
+    assert attn.attn_decode_splits(64, 32, 16, 8192, 128) == 1     # groups of 2: VALU kernel
     assert attn.attn_decode_splits(4, 32, 16, 8192, 128) == 8
     assert attn.attn_decode_splits(64, 32, 8, 8192, 128) == 1
     assert attn.attn_decode_splits(4, 32, 8, 8192, 128) == 16
