@@ -55,12 +55,6 @@ __device__ __forceinline__ float half_swap_max(float v) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ u32x4_t buffer_load_b128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
-}
-__device__ __forceinline__ u32x2_t buffer_load_b64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
-}
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -76,12 +70,6 @@ __device__ __forceinline__ void buffer_load_lds_b128(__amdgpu_buffer_rsrc_t r, u
 __device__ __forceinline__ void buffer_load_lds_b128_stream(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds_base) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 16, (int)voff, 0, 0, 2 /* nt */);
 }
-
-// Workgroup barrier without a memory fence.  __syncthreads() also waits for
-// every outstanding vector-memory operation, which would drain the LDS DMA
-// prefetch ring; callers that only need LDS data published wait for the DMA
-// they depend on with wait_vmcnt and have no LDS reads in flight.
-__device__ __forceinline__ void barrier_nofence() { __builtin_amdgcn_s_barrier(); }
 
 // s_waitcnt vmcnt(N) (other counters untouched); gfx9 encoding of the immediate.
 template <int N>
@@ -112,30 +100,6 @@ __device__ __forceinline__ void lgkm_wait_4(u32x2_t& a, u32x2_t& b, u32x2_t& c, 
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
 }
 
-// s_waitcnt lgkmcnt(0) + vmcnt(N) (LDS traffic drained, LDS DMA up to N pending).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_lgkm0() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N & 0x30) << 10) | (0x7 << 4));
-}
-
-// ds_read_b128 as inline asm, for the same reason as the transposed read.
-template <int OFF>
-__device__ __forceinline__ u32x4_t lds_read_b128(uint32_t addr) {
-    u32x4_t v;
-    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
-    return v;
-}
-// s_waitcnt lgkmcnt(0) with eight 16-byte results flowing through it.
-__device__ __forceinline__ void lgkm_wait_b128x8(u32x4_t* a) {
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]));
-}
-// s_waitcnt lgkmcnt(N) with four 16-byte results flowing through it.
-template <int N>
-__device__ __forceinline__ void lgkm_wait_b128x4(u32x4_t& a, u32x4_t& b, u32x4_t& c, u32x4_t& d) {
-    asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "i"(N));
-}
 
 // DPP row-local exchanges: lanes are paired within rows of 16.
 template <int CTRL>

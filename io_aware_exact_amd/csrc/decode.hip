@@ -575,12 +575,9 @@ hipError_t launch_mfma(const DecodeArgs& a, hipStream_t stream, const char** nam
 template <int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t stream, const char** name) {
     if (a.H / a.Hkv >= kMfmaMinGroup) return launch_mfma<D>(a, stream, name);
-    switch (head_tile(a.H / a.Hkv)) {
-        case 8: return launch_dg<D, 8>(a, stream, name);
-        case 4: return launch_dg<D, 4>(a, stream, name);
-        case 2: return launch_dg<D, 2>(a, stream, name);
-        default: return launch_dg<D, 1>(a, stream, name);
-    }
+    // below kMfmaMinGroup the head tile is 2 (groups of 2) or 1
+    if (head_tile(a.H / a.Hkv) == 2) return launch_dg<D, 2>(a, stream, name);
+    return launch_dg<D, 1>(a, stream, name);
 }
 
 }  // namespace
