@@ -697,7 +697,8 @@ def achievable_ceilings(torch):
     return out
 
 
-ISSUE_MODES = ("exp2_mul", "fma_mul", "mfma", "mfma_beside_exp2", "mfma_beside_fma", "prefill_block_mix")
+ISSUE_MODES = ("exp2_mul", "fma_mul", "mfma", "mfma_beside_exp2", "mfma_beside_fma", "prefill_block_mix",
+               "lds_read_b128", "lds_read_b64_tr_b16")
 ISSUE_OPS = {"exp2_mul": 16, "fma_mul": 16, "mfma": 2}   # independent ops per loop iteration
 
 
@@ -709,10 +710,11 @@ def instruction_rates(torch, waves=(1, 2, 3), rounds: int = 8):
     event-timed launch over the wave-iterations each SIMD ran, times the clock
     the waves' s_memtime / s_memrealtime ratio shows), and that clock.  Derived
     at 3 waves per SIMD (the prefill kernels' occupancy): cycles per exp2+mul
-    pair, per fma+mul pair, per 32x32x16 bf16 MFMA, and the share of the
+    pair, per fma+mul pair, per 32x32x16 bf16 MFMA, the share of the
     prefill's per-block mix (16 MFMAs and the softmax of 32 scores per lane,
-    from registers) that the matrix pipe is busy.  None if the probe library
-    is not built."""
+    from registers) that the matrix pipe is busy, and the LDS read rate of a
+    compute unit (conflict-free ds_read_b128, and ds_read_b64_tr_b16).  None if the probe library is
+    not built."""
     import ctypes
 
     path = os.path.join(ROOT, "io_aware_exact_amd", "libattn_probe.so")
@@ -763,6 +765,9 @@ def instruction_rates(torch, waves=(1, 2, 3), rounds: int = 8):
         "cycles_per_fma_mul": cycles["fma_mul"][w3] / ISSUE_OPS["fma_mul"],
         "cycles_per_mfma_32x32x16_bf16": mfma,
         "prefill_block_mix_mfma_share": 16 * mfma / cycles["prefill_block_mix"][w3],
+        # 4 SIMDs each finish one wave-iteration of 8 KiB of reads per that many cycles
+        "lds_read_bytes_per_clk_per_cu": 4 * 8192 / cycles["lds_read_b128"][w3],
+        "lds_read_tr_bytes_per_clk_per_cu": 4 * 8192 / cycles["lds_read_b64_tr_b16"][w3],
         "probe": ("instruction-mix probe (libattn_probe.so, issue_probe.hip): loops with no memory traffic, "
                   "w waves per SIMD held by an LDS reservation; modes " + ", ".join(ISSUE_MODES)),
     }
@@ -965,7 +970,9 @@ def main():
             iss = ceil["issue"]
             log(f"[bench] issue probe (3 waves/SIMD): exp2+mul {iss['cycles_per_exp2_mul']:.2f}, fma+mul "
                 f"{iss['cycles_per_fma_mul']:.2f}, MFMA {iss['cycles_per_mfma_32x32x16_bf16']:.1f} cycles; "
-                f"prefill block mix keeps the matrix pipe {100 * iss['prefill_block_mix_mfma_share']:.0f}% busy")
+                f"prefill block mix keeps the matrix pipe {100 * iss['prefill_block_mix_mfma_share']:.0f}% busy; "
+                f"LDS reads {iss['lds_read_bytes_per_clk_per_cu']:.0f} B/clk per CU "
+                f"({iss['lds_read_tr_bytes_per_clk_per_cu']:.0f} transposing)")
     if args.copy_calibration:
         result["copy_calibration_bytes"] = copy_calibration(torch)
     result["kernel_sources_digest"] = kernel_sources_digest()

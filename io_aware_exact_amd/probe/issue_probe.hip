@@ -18,6 +18,12 @@
 //      registers: 8 QK MFMAs, the softmax of 32 scores per lane (FMA, exp2,
 //      row-sum adds, bf16 packs) and 8 PV MFMAs, with the kernel's data
 //      dependences (the loop-carried accumulators and reference)
+//   6  8 ds_read_b128 (1 KiB per wave each, consecutive 16-byte chunks per
+//      lane: no bank conflicts) from the workgroup's LDS reservation, the
+//      LDS read rate
+//   7  the same 8 KiB per wave as 16 ds_read_b64_tr_b16: the transposing
+//      read, with the head-width-64 prefill's V operand addressing (a 64-row
+//      tile of 128-byte rows, 16-byte chunks XOR-swizzled by row bit 1)
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -33,6 +39,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 
@@ -51,6 +58,11 @@ void issue_probe_kernel(int iters, const u32x4_t* __restrict__ operands, float* 
                         long long* __restrict__ ticks) {
     __shared__ float reserve[reserve_floats(W)];   // occupancy limiter only
     const int tid = threadIdx.x;
+    if constexpr (MODE == 6 || MODE == 7) {
+        // fill the reservation once: the reads below see defined values
+        for (int i = tid; i < reserve_floats(W); i += kThreads) reserve[i] = (float)(i & 255);
+        __syncthreads();
+    }
     if (iters < 0) {                     // never taken: keeps the reservation
         reserve[tid] = 0.f;
         __syncthreads();
@@ -89,10 +101,41 @@ void issue_probe_kernel(int iters, const u32x4_t* __restrict__ operands, float* 
             if constexpr (MODE == 4) c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[1], q[1], c1, 0, 0, 0);
 #pragma unroll
             for (int i = 8; i < 16; ++i) x[i] = __builtin_fmaf(x[i], -0.5f, 0.25f) * -0.5f;
+        } else if constexpr (MODE == 6) {
+            // 8 KiB per wave per iteration; the offset walks the reservation
+            constexpr int CHUNKS = reserve_floats(W) / 4;          // 16-byte chunks
+            const u32x4_t* lds = reinterpret_cast<const u32x4_t*>(reserve);
+            const int base = ((tid >> 6) * 512 + it * 64) % CHUNKS;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const u32x4_t v = lds[(base + 64 * i + (tid & 63)) % CHUNKS];
+                x[2 * i] += __builtin_bit_cast(float, v[0] ^ v[1]);
+                x[2 * i + 1] += __builtin_bit_cast(float, v[2] ^ v[3]);
+            }
+        } else if constexpr (MODE == 7) {
+            // lane group lg = lane / 16 and jj = lane % 16 address row
+            // 4(lg/2) + jj/4 and columns 32dt + 16(lg%2) + 4(jj%4) of the tile;
+            // steps st = 0..3 add 16 rows, the second read of a pair 8 rows
+            const int lane = tid & 63, lg = lane >> 4, jj = lane & 15;
+            const int row = 4 * (lg >> 1) + (jj >> 2);
+            const int tile = ((tid >> 6) + it) % (reserve_floats(W) / 2048);   // 8 KiB tiles
+            __attribute__((address_space(3))) char* t0 =
+                reinterpret_cast<__attribute__((address_space(3))) char*>(
+                    (__attribute__((address_space(3))) float*)reserve) + 8192 * tile;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int st = i >> 2, dt = (i >> 1) & 1, half = i & 1;
+                const int col = 32 * dt + 16 * (lg & 1) + 4 * (jj & 3);
+                const int off = (16 * st + 8 * half + row) * 128 +
+                                ((((col >> 3) ^ (((row >> 1) & 1) << 2)) << 4) | ((col & 4) << 1));
+                const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    reinterpret_cast<__attribute__((address_space(3))) i16x4_t*>(t0 + off));
+                x[i] += (float)(v[0] ^ v[1] ^ v[2] ^ v[3]);
+            }
         } else if constexpr (MODE == 2) {
             c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[0], q[0], c0, 0, 0, 0);
             c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[1], q[1], c1, 0, 0, 0);
-        } else {
+        } else {   // 5
             asm volatile("" : "+v"(k[0]), "+v"(k[4]));   // opaque every iteration: nothing is hoisted
             f32x16_t s0 = {}, s1 = {};
 #pragma unroll
@@ -156,7 +199,7 @@ extern "C" {
 
 // Number of modes, and the bf16x8 operand words the caller provides
 // (20 per lane of a wave: 20 * 64 * 16 bytes).
-int probe_issue_modes(void) { return 6; }
+int probe_issue_modes(void) { return 8; }
 int probe_issue_operand_bytes(void) { return 20 * 64 * 16; }
 int probe_issue_threads(void) { return kThreads; }
 
@@ -168,7 +211,7 @@ int probe_issue_threads(void) { return kThreads; }
 // hipError_t of the launch; invalid arguments are refused before any launch.
 int probe_issue(int mode, int waves, int blocks, int iters, const void* operands, float* out, long long* ticks,
                 hipStream_t stream) {
-    if (mode < 0 || mode > 5 || waves < 1 || waves > 3 || blocks < 1 || iters < 1 || !operands || !out || !ticks)
+    if (mode < 0 || mode > 7 || waves < 1 || waves > 3 || blocks < 1 || iters < 1 || !operands || !out || !ticks)
         return (int)hipErrorInvalidValue;
     const u32x4_t* ops = static_cast<const u32x4_t*>(operands);
     switch (mode) {
@@ -177,7 +220,9 @@ int probe_issue(int mode, int waves, int blocks, int iters, const void* operands
         case 2: return (int)launch_mode<2>(waves, blocks, iters, ops, out, ticks, stream);
         case 3: return (int)launch_mode<3>(waves, blocks, iters, ops, out, ticks, stream);
         case 4: return (int)launch_mode<4>(waves, blocks, iters, ops, out, ticks, stream);
-        default: return (int)launch_mode<5>(waves, blocks, iters, ops, out, ticks, stream);
+        case 5: return (int)launch_mode<5>(waves, blocks, iters, ops, out, ticks, stream);
+        case 6: return (int)launch_mode<6>(waves, blocks, iters, ops, out, ticks, stream);
+        default: return (int)launch_mode<7>(waves, blocks, iters, ops, out, ticks, stream);
     }
 }
 
