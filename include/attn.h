@@ -148,8 +148,9 @@ size_t attn_decode_workspace_bytes(int B, int H, int d, int num_splits);
  * attn_decode_splits -- the number of key partitions the library picks for a
  * decode step (num_splits = 0): enough for about 512 workgroups (at most 16
  * partitions; 64 for groups of 4 or more query heads, whose kernel runs one
- * wave per workgroup), and none holding less than 64 KiB of K and V
- * (16384/d keys).  A single sequence offers only H
+ * wave per workgroup; grids of fewer than 16 head tiles take one workgroup
+ * per compute unit, 256 / tiles partitions, at most 64), and none holding
+ * less than 64 KiB of K and V (16384/d keys).  A single sequence offers only H
  * independent heads, too few to occupy the chip; splitting the key axis is
  * the remedy "Attention and Its Computational Cost" proposes for its batch-1
  * decode measurement ("The other shape: one query, many keys").  Returns 0

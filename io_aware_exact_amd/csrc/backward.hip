@@ -76,15 +76,26 @@ template <int D, int STP>
 __device__ __forceinline__ void tr_kstep(uint32_t base, const uint32_t (&o)[D / 32][2], u32x4_t (&a)[D / 32]) {
     constexpr int OFF = STP * 16 * D * 2;
 #pragma unroll
-    for (int d2 = 0; d2 < D / 32; d2 += 2) {
-        u32x2_t l0 = lds_read_tr16_b64<OFF>(base + o[d2][0]);
-        u32x2_t h0 = lds_read_tr16_b64<OFF>(base + o[d2][1]);
-        u32x2_t l1 = lds_read_tr16_b64<OFF>(base + o[d2 + 1][0]);
-        u32x2_t h1 = lds_read_tr16_b64<OFF>(base + o[d2 + 1][1]);
-        lgkm_wait_4(l0, h0, l1, h1);
-        a[d2] = u32x4_t{l0[0], l0[1], h0[0], h0[1]};
-        a[d2 + 1] = u32x4_t{l1[0], l1[1], h1[0], h1[1]};
-    }
+    for (int d2 = 0; d2 < D / 32; d2 += 2)
+        lds_read_tr16_x4<OFF, OFF, OFF, OFF>(base + o[d2][0], base + o[d2][1], base + o[d2 + 1][0],
+                                             base + o[d2 + 1][1], a[d2], a[d2 + 1]);
+}
+
+// Head width 64: the transposed operands of two k-steps at once (k-step S0 of
+// the 32-row group at `base0`, k-step S1 of the group at `base1`) behind one
+// wait.
+template <int S0, int S1>
+__device__ __forceinline__ void tr_kstep2_d64(uint32_t base0, uint32_t base1, const uint32_t (&o)[2][2],
+                                              u32x4_t (&a0)[2], u32x4_t (&a1)[2]) {
+    constexpr int F0 = S0 * 16 * 64 * 2, F1 = S1 * 16 * 64 * 2;
+    const uint32_t ad[8] = {base0 + o[0][0], base0 + o[0][1], base0 + o[1][0], base0 + o[1][1],
+                            base1 + o[0][0], base1 + o[0][1], base1 + o[1][0], base1 + o[1][1]};
+    u32x4_t r[4];
+    lds_read_tr16_x8<F0, F0, F0, F0, F1, F1, F1, F1>(ad, r);
+    a0[0] = r[0];
+    a0[1] = r[1];
+    a1[0] = r[2];
+    a1[1] = r[3];
 }
 
 // Transposed-read offsets of a lane: lane group lg = lane / 16, jj = lane % 16
@@ -259,11 +270,13 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                 const float lse2 = (i < 2) ? st0[2 * i] : st1[2 * (i - 2)];
                 const float dd = (i < 2) ? st0[2 * i + 1] : st1[2 * (i - 2) + 1];
                 const int r = 4 * g4 + i;
-                float pe = fast_exp2(__builtin_fmaf(s[r], c, -lse2));
+                float x = __builtin_fmaf(s[r], c, -lse2);
                 if constexpr (MASK) {
+                    // a masked score gets exponent -inf: exp2 gives 0, no branch
                     const int qrow = q0 + rb + i;
-                    if (qrow >= Tq || (CAUSAL && key > qrow + off)) pe = 0.f;
+                    x = (qrow >= Tq || (CAUSAL && key > qrow + off)) ? -__builtin_inff() : x;
                 }
+                const float pe = fast_exp2(x);
                 p[i] = pe;
                 ds[i] = pe * (dp[r] - dd);
             }
@@ -281,17 +294,32 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
             const u32x4_t dv = {dw[4 * stp], dw[4 * stp + 1], dw[4 * stp + 2], dw[4 * stp + 3]};
             const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pv);
             const bf16x8_t db = __builtin_bit_cast(bf16x8_t, dv);
-            u32x4_t a[DT];
-            tr_kstep<D, stp>(gb, t_off, a);
+            if constexpr (D == 64 && QS > 1) {
+                // dO^T and Q^T operands of this k-step behind one wait (the
+                // 8 extra registers would make QS = 1 spill)
+                u32x4_t ag[2], aq[2];
+                tr_kstep2_d64<stp, stp>(gb, qb, t_off, ag, aq);
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-                dvt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[dt]), pb, dvt[dt],
-                                                                  0, 0, 0);
-            tr_kstep<D, stp>(qb, t_off, a);
+                for (int dt = 0; dt < 2; ++dt)
+                    dvt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ag[dt]), pb,
+                                                                      dvt[dt], 0, 0, 0);
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-                dkt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[dt]), db, dkt[dt],
-                                                                  0, 0, 0);
+                for (int dt = 0; dt < 2; ++dt)
+                    dkt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, aq[dt]), db,
+                                                                      dkt[dt], 0, 0, 0);
+            } else {
+                u32x4_t a[DT];
+                tr_kstep<D, stp>(gb, t_off, a);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+                    dvt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[dt]), pb,
+                                                                      dvt[dt], 0, 0, 0);
+                tr_kstep<D, stp>(qb, t_off, a);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+                    dkt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[dt]), db,
+                                                                      dkt[dt], 0, 0, 0);
+            }
         };
         kstep(std::integral_constant<int, 0>{});
         kstep(std::integral_constant<int, 1>{});
@@ -518,12 +546,13 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
             float ds[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float pe = fast_exp2(__builtin_fmaf(s[r], c, -lse2));
+                float x = __builtin_fmaf(s[r], c, -lse2);
                 if constexpr (MASK) {
+                    // a masked score gets exponent -inf: exp2 gives 0, no branch
                     const int kk = kb + 32 * kt + 8 * (r >> 2) + 4 * hf + (r & 3);
-                    if (kk > lim) pe = 0.f;
+                    x = kk > lim ? -__builtin_inff() : x;
                 }
-                ds[r] = pe * (dp[r] - dd);
+                ds[r] = fast_exp2(x) * (dp[r] - dd);
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) dw[8 * kt + i] = pack_bf16x2(ds[2 * i], ds[2 * i + 1]);
@@ -541,11 +570,32 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                 dqt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[dt]), db, dqt[dt],
                                                                   0, 0, 0);
         };
-        kstep(std::integral_constant<int, 0>{});
-        kstep(std::integral_constant<int, 1>{});
-        if constexpr (WKT > 1) {
-            kstep(std::integral_constant<int, 2>{});
-            kstep(std::integral_constant<int, 3>{});
+        // head width 64: two k-steps' K^T operands behind one wait
+        auto kstep_pair = [&](auto stp_tag) {
+            constexpr int stp = decltype(stp_tag)::value;
+            u32x4_t a0[2], a1[2];
+            tr_kstep2_d64<stp, stp + 1>(kbase, kbase, t_off, a0, a1);
+            const u32x4_t d0 = {dw[4 * stp], dw[4 * stp + 1], dw[4 * stp + 2], dw[4 * stp + 3]};
+            const u32x4_t d1 = {dw[4 * stp + 4], dw[4 * stp + 5], dw[4 * stp + 6], dw[4 * stp + 7]};
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt)
+                dqt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a0[dt]),
+                                                                  __builtin_bit_cast(bf16x8_t, d0), dqt[dt], 0, 0, 0);
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt)
+                dqt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a1[dt]),
+                                                                  __builtin_bit_cast(bf16x8_t, d1), dqt[dt], 0, 0, 0);
+        };
+        if constexpr (D == 64) {
+            kstep_pair(std::integral_constant<int, 0>{});
+            if constexpr (WKT > 1) kstep_pair(std::integral_constant<int, 2>{});
+        } else {
+            kstep(std::integral_constant<int, 0>{});
+            kstep(std::integral_constant<int, 1>{});
+            if constexpr (WKT > 1) {
+                kstep(std::integral_constant<int, 2>{});
+                kstep(std::integral_constant<int, 3>{});
+            }
         }
     };
 

@@ -85,19 +85,50 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
 // (i % 4) of the 8-byte pieces addressed by lanes 4r + i/4, r = 0..3.
-// Issued as inline asm because the compiler would otherwise wait for every
-// outstanding LDS DMA before it (it cannot see that the rings' stages do not
-// overlap); the caller must pass the results through lgkm_wait_* before use.
-template <int OFF>
-__device__ __forceinline__ u32x2_t lds_read_tr16_b64(uint32_t addr) {
-    u32x2_t v;
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
-    return v;
+// Four of them, at per-lane LDS addresses a0..a3 plus the immediate offsets
+// O0..O3, and the wait for them, in one asm statement: the results are
+// complete before the compiler can read or reuse their registers, and the
+// outputs are early-clobber so no address register is overwritten while a
+// read is in flight.  r0 = (read 0, read 1) and r1 = (read 2, read 3), two
+// MFMA operands.  Inline asm because the compiler would otherwise wait for
+// every outstanding LDS DMA before each read (it cannot see that the rings'
+// stages do not overlap).
+template <int O0, int O1, int O2, int O3>
+__device__ __forceinline__ void lds_read_tr16_x4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, u32x4_t& r0,
+                                                 u32x4_t& r1) {
+    u32x2_t v0, v1, v2, v3;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4 offset:%8\n\t"
+        "ds_read_b64_tr_b16 %1, %5 offset:%9\n\t"
+        "ds_read_b64_tr_b16 %2, %6 offset:%10\n\t"
+        "ds_read_b64_tr_b16 %3, %7 offset:%11\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
+        : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "i"(O0), "i"(O1), "i"(O2), "i"(O3));
+    r0 = u32x4_t{v0[0], v0[1], v1[0], v1[1]};
+    r1 = u32x4_t{v2[0], v2[1], v3[0], v3[1]};
 }
-// s_waitcnt lgkmcnt(0) that the given registers flow through, so nothing that
-// reads them can be scheduled before the wait.
-__device__ __forceinline__ void lgkm_wait_4(u32x2_t& a, u32x2_t& b, u32x2_t& c, u32x2_t& d) {
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+// Eight of them and one wait, the same way: r[i] = (read 2i, read 2i + 1).
+template <int O0, int O1, int O2, int O3, int O4, int O5, int O6, int O7>
+__device__ __forceinline__ void lds_read_tr16_x8(const uint32_t (&a)[8], u32x4_t (&r)[4]) {
+    u32x2_t v0, v1, v2, v3, v4, v5, v6, v7;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %1, %9 offset:%17\n\t"
+        "ds_read_b64_tr_b16 %2, %10 offset:%18\n\t"
+        "ds_read_b64_tr_b16 %3, %11 offset:%19\n\t"
+        "ds_read_b64_tr_b16 %4, %12 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %5, %13 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %6, %14 offset:%22\n\t"
+        "ds_read_b64_tr_b16 %7, %15 offset:%23\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3), "=&v"(v4), "=&v"(v5), "=&v"(v6), "=&v"(v7)
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "i"(O0), "i"(O1),
+          "i"(O2), "i"(O3), "i"(O4), "i"(O5), "i"(O6), "i"(O7));
+    r[0] = u32x4_t{v0[0], v0[1], v1[0], v1[1]};
+    r[1] = u32x4_t{v2[0], v2[1], v3[0], v3[1]};
+    r[2] = u32x4_t{v4[0], v4[1], v5[0], v5[1]};
+    r[3] = u32x4_t{v6[0], v6[1], v7[0], v7[1]};
 }
 
 

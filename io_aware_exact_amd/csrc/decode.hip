@@ -30,6 +30,7 @@
 //
 // Partial record per (batch*query head, partition): o (D floats, not
 // normalised), then m (max of scale*log2e*q.k) and l, all fp32.
+#include <algorithm>
 #include <cstdio>
 #include <mutex>
 
@@ -452,21 +453,12 @@ void decode_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
             const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pv);
 #pragma unroll
             for (int d2 = 0; d2 < DT; d2 += 2) {
-                u32x2_t l0, h0, l1, h1;
-                if (st == 0) {
-                    l0 = lds_read_tr16_b64<0>(vb + v_roff[d2]);
-                    h0 = lds_read_tr16_b64<8 * ROWB>(vb + v_roff[d2]);
-                    l1 = lds_read_tr16_b64<0>(vb + v_roff[d2 + 1]);
-                    h1 = lds_read_tr16_b64<8 * ROWB>(vb + v_roff[d2 + 1]);
-                } else {
-                    l0 = lds_read_tr16_b64<16 * ROWB>(vb + v_roff[d2]);
-                    h0 = lds_read_tr16_b64<24 * ROWB>(vb + v_roff[d2]);
-                    l1 = lds_read_tr16_b64<16 * ROWB>(vb + v_roff[d2 + 1]);
-                    h1 = lds_read_tr16_b64<24 * ROWB>(vb + v_roff[d2 + 1]);
-                }
-                lgkm_wait_4(l0, h0, l1, h1);
-                const u32x4_t a0 = {l0[0], l0[1], h0[0], h0[1]};
-                const u32x4_t a1 = {l1[0], l1[1], h1[0], h1[1]};
+                const uint32_t va = vb + v_roff[d2], vc = vb + v_roff[d2 + 1];
+                u32x4_t a0, a1;
+                if (st == 0)
+                    lds_read_tr16_x4<0, 8 * ROWB, 0, 8 * ROWB>(va, va, vc, vc, a0, a1);
+                else
+                    lds_read_tr16_x4<16 * ROWB, 24 * ROWB, 16 * ROWB, 24 * ROWB>(va, va, vc, vc, a0, a1);
                 oacc[d2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a0), pb, oacc[d2],
                                                                    0, 0, 0);
                 oacc[d2 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a1), pb,
@@ -582,13 +574,20 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t stream, const char** name) 
 
 }  // namespace
 
+constexpr long long kCUs = 256;   // compute units of an MI355X
+
 int decode_auto_splits(int B, int Hq, int Hkv, int Tkv, int d) {
     // Enough partitions for about 512 workgroups (2 per CU), each holding at
     // least 64 KiB of K and V (256 keys at d = 64, 128 at d = 128); at most 16
     // partitions for the 8-wave VALU kernel and 64 for the 1-wave MFMA kernel.
     // Measured on 12 heads of 64 and 32 heads of 128, groups of 1-32, batch
     // 1-64, 128-16K keys: shorter or more numerous partitions lose to their
-    // start-up latency and the merge.
+    // start-up latency and the merge.  A VALU grid that 16 partitions leave
+    // below one workgroup per CU (fewer than 16 head tiles) takes as many as
+    // fill the CUs once, up to 64: more than one per CU would leave some CUs
+    // a second workgroup to run after the rest have finished (batch 1, 16K
+    // keys: 12 heads 12.4 -> 11.8 us at 21 partitions, 8 heads of 128
+    // 17.0 -> 13.8 us at 32, 4 heads of 128 26.2 -> 15.7 us at 64).
     const int G = Hq / Hkv;
     const bool mfma = G >= kMfmaMinGroup;
     const long long wgs = mfma ? (long long)B * Hkv * ((G + 31) / 32) : (long long)B * Hkv * (G / head_tile(G));
@@ -596,7 +595,8 @@ int decode_auto_splits(int B, int Hq, int Hkv, int Tkv, int d) {
     const int min_keys = 16384 / d;
     int p = 1;
     while (p < cap && wgs * p < 512) p *= 2;
-    while (p > 1 && Tkv / p < min_keys) p /= 2;
+    if (!mfma && wgs * p < kCUs) p = (int)std::min<long long>(64, kCUs / wgs);
+    p = std::min(p, std::max(1, Tkv / min_keys));
     return p;
 }
 

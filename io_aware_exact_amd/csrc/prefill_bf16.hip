@@ -411,13 +411,9 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
             const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pv);
 #pragma unroll
             for (int d2 = 0; d2 < DT; d2 += 2) {
-                u32x2_t lo0 = lds_read_tr16_b64<o>(vbase + v_roff[d2]);
-                u32x2_t hi0 = lds_read_tr16_b64<o + 8 * ROWB>(vbase + v_roff[d2]);
-                u32x2_t lo1 = lds_read_tr16_b64<o>(vbase + v_roff[d2 + 1]);
-                u32x2_t hi1 = lds_read_tr16_b64<o + 8 * ROWB>(vbase + v_roff[d2 + 1]);
-                lgkm_wait_4(lo0, hi0, lo1, hi1);
-                const u32x4_t a0 = {lo0[0], lo0[1], hi0[0], hi0[1]};
-                const u32x4_t a1 = {lo1[0], lo1[1], hi1[0], hi1[1]};
+                const uint32_t va = vbase + v_roff[d2], vc = vbase + v_roff[d2 + 1];
+                u32x4_t a0, a1;
+                lds_read_tr16_x4<o, o + 8 * ROWB, o, o + 8 * ROWB>(va, va, vc, vc, a0, a1);
                 oacc[d2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a0), pb, oacc[d2],
                                                                    0, 0, 0);
                 oacc[d2 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a1), pb,
@@ -508,13 +504,9 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
             const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pv);
 #pragma unroll
             for (int d2 = 0; d2 < DT; d2 += 2) {
-                u32x2_t lo0 = lds_read_tr16_b64<SO + o>(v_ra1[d2]);
-                u32x2_t hi0 = lds_read_tr16_b64<SO + o + 8 * ROWB>(v_ra1[d2]);
-                u32x2_t lo1 = lds_read_tr16_b64<SO + o>(v_ra1[d2 + 1]);
-                u32x2_t hi1 = lds_read_tr16_b64<SO + o + 8 * ROWB>(v_ra1[d2 + 1]);
-                lgkm_wait_4(lo0, hi0, lo1, hi1);
-                const u32x4_t a0 = {lo0[0], lo0[1], hi0[0], hi0[1]};
-                const u32x4_t a1 = {lo1[0], lo1[1], hi1[0], hi1[1]};
+                u32x4_t a0, a1;
+                lds_read_tr16_x4<SO + o, SO + o + 8 * ROWB, SO + o, SO + o + 8 * ROWB>(
+                    v_ra1[d2], v_ra1[d2], v_ra1[d2 + 1], v_ra1[d2 + 1], a0, a1);
                 oacc[d2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a0), pb, oacc[d2],
                                                                    0, 0, 0);
                 oacc[d2 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a1), pb,
@@ -609,16 +601,14 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
                 }
             }
             constexpr int VO = S * STAGEB;
-            u32x2_t vr[2][2][2];
-            vr[0][0][0] = lds_read_tr16_b64<VO>(v_ra[0]);
-            vr[0][0][1] = lds_read_tr16_b64<VO + 8 * ROWB>(v_ra[0]);
-            vr[0][1][0] = lds_read_tr16_b64<VO>(v_ra[1]);
-            vr[0][1][1] = lds_read_tr16_b64<VO + 8 * ROWB>(v_ra[1]);
-            vr[1][0][0] = lds_read_tr16_b64<VO + 16 * ROWB>(v_ra[0]);
-            vr[1][0][1] = lds_read_tr16_b64<VO + 24 * ROWB>(v_ra[0]);
-            vr[1][1][0] = lds_read_tr16_b64<VO + 16 * ROWB>(v_ra[1]);
-            vr[1][1][1] = lds_read_tr16_b64<VO + 24 * ROWB>(v_ra[1]);
             nxt = qk(std::integral_constant<int, S1>{});   // past the last block: unused
+            // this block's V operands (both 16-key steps), read while the
+            // matrix pipe runs the next block's QK products
+            u32x4_t va[2][2];
+            lds_read_tr16_x4<VO, VO + 8 * ROWB, VO, VO + 8 * ROWB>(v_ra[0], v_ra[0], v_ra[1], v_ra[1], va[0][0],
+                                                                   va[0][1]);
+            lds_read_tr16_x4<VO + 16 * ROWB, VO + 24 * ROWB, VO + 16 * ROWB, VO + 24 * ROWB>(
+                v_ra[0], v_ra[0], v_ra[1], v_ra[1], va[1][0], va[1][1]);
             uint32_t pw[8];
             float rs = 0.f;
             auto exponentiate = [&](float mref) {
@@ -653,16 +643,13 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
                 exponentiate(m_use);
             }
             l += rs;
-            lgkm_wait_4(vr[0][0][0], vr[0][0][1], vr[0][1][0], vr[0][1][1]);
-            lgkm_wait_4(vr[1][0][0], vr[1][0][1], vr[1][1][0], vr[1][1][1]);
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
                 const u32x4_t pv = {pw[4 * st], pw[4 * st + 1], pw[4 * st + 2], pw[4 * st + 3]};
                 const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pv);
 #pragma unroll
                 for (int dt = 0; dt < 2; ++dt) {
-                    const u32x4_t a = {vr[st][dt][0][0], vr[st][dt][0][1], vr[st][dt][1][0], vr[st][dt][1][1]};
-                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), pb,
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va[st][dt]), pb,
                                                                        oacc[dt], 0, 0, 0);
                 }
             }

@@ -222,7 +222,11 @@ def test_decode_automatic_splits():
     # 12 heads of one sequence: 512 workgroups would need 43 partitions; capped at 16
     # (8-wave workgroups), then halved until partitions hold >= 64 KiB of K+V (256 keys
     # at d=64, 128 at d=128)
-    assert attn.attn_decode_splits(1, 12, 12, 16384, 64) == 16
+    assert attn.attn_decode_splits(1, 12, 12, 16384, 64) == 21   # 12 workgroups: one per CU
+    assert attn.attn_decode_splits(1, 8, 8, 16384, 64) == 32
+    assert attn.attn_decode_splits(1, 4, 4, 32768, 128) == 64
+    assert attn.attn_decode_splits(1, 12, 12, 3000, 64) == 11     # partitions of at least 256 keys
+    assert attn.attn_decode_splits(2, 12, 12, 16384, 64) == 16    # 24 workgroups: 384 at 16
     assert attn.attn_decode_splits(1, 12, 12, 4096, 64) == 16
     assert attn.attn_decode_splits(1, 12, 12, 1024, 64) == 4
     assert attn.attn_decode_splits(1, 12, 12, 300, 64) == 1
