@@ -813,6 +813,256 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
     }
 }
 
+// Head width 64, full attention, 256-row tiles.  Each of the 4 waves owns 64
+// query rows as two 32-row sub-tiles u = 0, 1 (rows 64w + 32u + ln) and all 64
+// keys of every stage, so every K and V operand it reads from LDS feeds both
+// sub-tiles: a query row pulls half the LDS operand bytes of
+// prefill_bf16_kernel, a wave's work per stage doubles (32 MFMAs, 2 x 32
+// scores per lane), and two waves fit per SIMD -- 512 resident tiles where the
+// 128-row kernel has 768.  Grids whose 128-row tiles would need a partly
+// filled last round use it.  Ring (3 stages), DMA mapping, swizzles, the lazy
+// reference max and the head-major tile order are prefill_bf16_kernel's; the
+// only element mask is the ragged end of the key axis.
+__global__ __launch_bounds__(256, 2)
+void prefill_bf16_d64_r256_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                  const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+                                  float* __restrict__ LSE, int Tq, int Tkv, int BH, int nqt, float c) {
+    using G = Geo<64>;
+    constexpr int D = 64, BK = 64, ROWB = 2 * D, TILEB = BK * ROWB, CPR = ROWB / 16, RPG = 1024 / ROWB;
+    constexpr int TQ = D / 16, DT = D / 32, KT = BK / 32, NS = 3, BQ = 256;
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[NS][2][TILEB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ln = lane & 31;
+    const int hf = lane >> 5;
+
+    const int id = blockIdx.x;
+    int bh, qt;
+    if ((BH & 7) == 0) {
+        // XCD x (block ids x, x+8, ...) runs its heads x, x+8, ... one after
+        // another, every tile of a head before the next head
+        const int xcd = id & 7, k = id >> 3;
+        qt = k % nqt;
+        bh = (k / nqt) * 8 + xcd;
+    } else {
+        bh = id % BH;
+        qt = id / BH;
+    }
+    const int q0 = qt * BQ;
+    const int nblk = (Tkv + BK - 1) / BK;
+    const int nfull = Tkv / BK;               // blocks with no key past the end
+
+    const size_t qbase = (size_t)bh * Tq * D;
+    const size_t kvbase = (size_t)bh * Tkv * D;
+    const uint16_t* Kh = K + kvbase;
+    const uint16_t* Vh = V + kvbase;
+
+    // Q fragments of the two sub-tiles: row q0 + 64w + 32u + ln, d = 16t + 8hf + (0..7)
+    bf16x8_t qf[2][TQ];
+    int qrow[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        qrow[u] = q0 + 64 * wave + 32 * u + ln;
+        if (qrow[u] < Tq) {
+            const u32x4_t* src = reinterpret_cast<const u32x4_t*>(Q + qbase + (size_t)qrow[u] * D + 8 * hf);
+#pragma unroll
+            for (int t = 0; t < TQ; ++t) qf[u][t] = __builtin_bit_cast(bf16x8_t, src[2 * t]);
+        } else {
+#pragma unroll
+            for (int t = 0; t < TQ; ++t) qf[u][t] = __builtin_bit_cast(bf16x8_t, u32x4_t{0, 0, 0, 0});
+        }
+    }
+
+    // DMA: wave w moves the 1 KiB row groups g0 and g0 + 2 of K and V, as in
+    // prefill_bf16_kernel (the second load is the first plus 2 KiB in the
+    // instruction's offset field)
+    const int g0 = (wave & 1) + 4 * (wave >> 1);
+    const int row0 = RPG * g0 + lane / CPR;
+    const uint32_t k_voff0 = (uint32_t)(row0 * ROWB + (((lane % CPR) ^ G::swz_k(row0)) << 4));
+    const uint32_t v_voff0 = (uint32_t)(row0 * ROWB + (((lane % CPR) ^ G::swz_v(row0)) << 4));
+    auto issue = [&](int j, auto stage_tag) {
+        constexpr int S = decltype(stage_tag)::value;
+        const uint32_t kb = (uint32_t)j * BK;
+        const uint32_t bytes = j < nblk ? (uint32_t)(Tkv - (int)kb) * (uint32_t)ROWB : 0u;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)kb * D, bytes);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (size_t)kb * D, bytes);
+        uint8_t* st = &ring[S][0][0] + g0 * 1024;
+        buffer_load_lds_b128_off<0>(rk, k_voff0, st);
+        buffer_load_lds_b128_off<2048>(rk, k_voff0, st);
+        buffer_load_lds_b128_off<0>(rv, v_voff0, st + TILEB);
+        buffer_load_lds_b128_off<2048>(rv, v_voff0, st + TILEB);
+    };
+
+    // per-lane LDS read addresses in stage 0: K operand of step t (row ln,
+    // chunk 2t + hf; kt adds 32 rows), V operand of d-tile dt (transposed read)
+    const uint32_t ring_lds = lds_addr(&ring[0][0][0]);
+    uint32_t k_ra[TQ], v_ra[DT];
+#pragma unroll
+    for (int t = 0; t < TQ; ++t) k_ra[t] = ring_lds + (uint32_t)(ln * ROWB + (((2 * t + hf) ^ G::swz_k(ln)) << 4));
+    {
+        const int lg = lane >> 4, jj = lane & 15;
+        const int row = 4 * (lg >> 1) + (jj >> 2);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const int col = 32 * dt + 16 * (lg & 1) + 4 * (jj & 3);
+            v_ra[dt] = ring_lds + TILEB +
+                       (uint32_t)(row * ROWB + ((((col >> 3) ^ G::swz_v(row)) << 4) | ((col & 4) << 1)));
+        }
+    }
+
+    f32x16_t oacc[2][DT];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[u][dt][r] = 0.f;
+    float m[2] = {kNegInf, kNegInf};
+    float l[2] = {0.f, 0.f};
+
+    // One 64-key stage as two 32-key halves kt, each QK -> softmax -> PV for
+    // both sub-tiles (two live score tiles instead of four; the lazy
+    // reference is checked per half, which any grouping of keys allows).
+    // One 64-key stage: QK for both sub-tiles (each K operand read feeds two
+    // MFMAs), the softmax of each, then PV (each V operand read feeds two).
+    auto step = [&](uint32_t so, int kb, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        f32x16_t s[2][KT];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[u][kt][r] = 0.f;
+        auto qk_tile = [&](auto kt_tag) {
+            constexpr int kt = decltype(kt_tag)::value;
+#pragma unroll
+            for (int t = 0; t < TQ; ++t) {
+                const bf16x8_t a = lds_load_b128<kt * 32 * ROWB>(k_ra[t] + so);
+                s[0][kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][t], s[0][kt], 0, 0, 0);
+                s[1][kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][t], s[1][kt], 0, 0, 0);
+            }
+        };
+        qk_tile(std::integral_constant<int, 0>{});
+        qk_tile(std::integral_constant<int, 1>{});
+        if constexpr (MASK) {
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kb + 32 * kt + 8 * (r >> 2) + 4 * hf + (r & 3);
+                    if (key >= Tkv) {
+                        s[0][kt][r] = kNegInf;
+                        s[1][kt][r] = kNegInf;
+                    }
+                }
+        }
+        uint32_t pw[2][8 * KT];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            float rs = 0.f;
+            auto exponentiate = [&](float mref) {
+                rs = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8 * KT; ++i) {
+                    const int kt = i >> 3, r = 2 * (i & 7);
+                    const float p0 = fast_exp2(__builtin_fmaf(s[u][kt][r], c, -mref));
+                    const float p1 = fast_exp2(__builtin_fmaf(s[u][kt][r + 1], c, -mref));
+                    pw[u][i] = pack_bf16x2(p0, p1);
+                    rs += p0 + p1;
+                }
+            };
+            exponentiate(m[u]);
+            const float row = half_swap_sum(rs);
+            if (__builtin_amdgcn_ballot_w64(!(row <= kSumLimit)) != 0) {
+                // raise the reference to the true running max and rescale
+                float mx = kNegInf;
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[u][kt][r]);
+                mx = half_swap_max(mx);
+                const float m_new = fmaxf(m[u], mx * c);
+                const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+                const float alpha = fast_exp2(m[u] - m_use);
+                l[u] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[u][dt][r] *= alpha;
+                m[u] = m_new;
+                exponentiate(m_use);
+            }
+            l[u] += rs;
+        }
+        // O^T += V^T bf16(P)^T over four 16-key steps; each V operand serves both sub-tiles
+        auto pv_step = [&](auto st_tag) {
+            constexpr int st = decltype(st_tag)::value;
+            constexpr int o = st * 16 * ROWB;
+            const uint32_t va = v_ra[0] + so, vc = v_ra[1] + so;
+            u32x4_t a0, a1;
+            lds_read_tr16_x4<o, o + 8 * ROWB, o, o + 8 * ROWB>(va, va, vc, vc, a0, a1);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const u32x4_t pv = {pw[u][4 * st], pw[u][4 * st + 1], pw[u][4 * st + 2], pw[u][4 * st + 3]};
+                const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pv);
+                oacc[u][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a0), pb,
+                                                                     oacc[u][0], 0, 0, 0);
+                oacc[u][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a1), pb,
+                                                                     oacc[u][1], 0, 0, 0);
+            }
+        };
+        pv_step(std::integral_constant<int, 0>{});
+        pv_step(std::integral_constant<int, 1>{});
+        pv_step(std::integral_constant<int, 2>{});
+        pv_step(std::integral_constant<int, 3>{});
+    };
+
+    // block j in stage j % 3: wait for it, free stage (j - 1) % 3 with the
+    // barrier, refill that stage with block j + 2
+    auto issue_rt = [&](int j) {
+        switch (j % 3) {
+            case 0: issue(j, std::integral_constant<int, 0>{}); break;
+            case 1: issue(j, std::integral_constant<int, 1>{}); break;
+            default: issue(j, std::integral_constant<int, 2>{}); break;
+        }
+    };
+    issue_rt(0);
+    issue_rt(1);
+    auto blk = [&](int j, auto mask_tag) {
+        wait_vmcnt<4 * (NS - 2)>();           // this wave's part of block j has landed
+        __syncthreads();                      // ... everyone's, and stage (j-1) % 3 is free
+        issue_rt(j + NS - 1);
+        step((uint32_t)(j % 3) * (2 * TILEB), j * BK, mask_tag);
+    };
+    int j = 0;
+    for (; j < nfull; ++j) blk(j, std::false_type{});
+    for (; j < nblk; ++j) blk(j, std::true_type{});
+    wait_vmcnt<0>();    // no DMA may still be writing LDS when the workgroup retires
+
+    // epilogue: divide once, write O (bf16) and LSE (fp32)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const float lsum = half_swap_sum(l[u]);
+        if (qrow[u] < Tq) {
+            const float inv = 1.0f / lsum;
+            uint16_t* orow = O + qbase + (size_t)qrow[u] * D;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const u32x2_t w = {pack_bf16x2(oacc[u][dt][4 * g] * inv, oacc[u][dt][4 * g + 1] * inv),
+                                       pack_bf16x2(oacc[u][dt][4 * g + 2] * inv, oacc[u][dt][4 * g + 3] * inv)};
+                    *reinterpret_cast<u32x2_t*>(orow + 32 * dt + 8 * g + 4 * hf) = w;
+                }
+            if (LSE != nullptr && hf == 0)
+                LSE[(size_t)bh * Tq + qrow[u]] = (m[u] + __builtin_log2f(lsum)) * 0.69314718055994530942f;
+        }
+    }
+}
+
 // Merge the chunk partials of each split tile: for row r with chunk results
 // (O_c, lse2_c), M = max_c lse2_c, w_c = 2^(lse2_c - M),
 // O = sum_c w_c O_c / sum_c w_c and LSE = (M + log2 sum_c w_c) ln 2 -- the
@@ -889,6 +1139,28 @@ bool use_key_halves(const PrefillArgs& a, int nch_max) {
     if (a.d != 64 || nch_max > 1) return false;
     const long long tiles = (long long)((a.Tq + kBQ - 1) / kBQ) * a.B * a.H;
     return tiles < 3LL * 256;
+}
+
+// The 256-row full-attention kernel (d = 64, unsplit, not key halves) where
+// its 512 resident tiles need fewer rounds than the 128-row kernel's 768:
+// there the 128-row grid ends in a partly filled round.
+bool use_rows256(const PrefillArgs& a, int nch_max) {
+    if (a.d != 64 || a.causal || nch_max > 1 || use_key_halves(a, nch_max)) return false;
+    const long long bh = (long long)a.B * a.H;
+    const long long rounds128 = ((a.Tq + kBQ - 1) / kBQ * bh + 3 * 256 - 1) / (3 * 256);
+    const long long rounds256 = ((a.Tq + 255) / 256 * bh + 2 * 256 - 1) / (2 * 256);
+    return rounds256 < rounds128;
+}
+
+hipError_t launch_rows256(const PrefillArgs& a, hipStream_t stream) {
+    const int nqt = (a.Tq + 255) / 256;
+    const long long grid = (long long)nqt * a.B * a.H;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(prefill_bf16_d64_r256_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                       static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, a.Tq, a.Tkv,
+                       a.B * a.H, nqt, a.c);
+    return hipGetLastError();
 }
 
 template <bool CAUSAL>
@@ -986,6 +1258,11 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, const PrefillSplit& sp, hip
                  a.causal ? ",causal" : "");
         *name = g_name;
         return a.causal ? launch_halves<true>(a, stream) : launch_halves<false>(a, stream);
+    }
+    if (use_rows256(a, sp.nch_max)) {
+        snprintf(g_name, sizeof g_name, "prefill_bf16_d64<waves=4,bq=256,bk=64,stages=3,rows_per_wave=64>");
+        *name = g_name;
+        return launch_rows256(a, stream);
     }
     if (sp.nch_max > 1)
         snprintf(g_name, sizeof g_name, "prefill_bf16_d%d<waves=4,bq=128,bk=%d,stages=3%s,kv_chunk=%d>+combine",

@@ -49,7 +49,8 @@ def capture(prepare):
     return graph
 
 
-@pytest.mark.parametrize("B,H,T,d,causal", [(2, 4, 300, 64, True), (1, 3, 200, 128, False), (8, 96, 129, 64, True)])
+@pytest.mark.parametrize("B,H,T,d,causal", [(2, 4, 300, 64, True), (1, 3, 200, 128, False), (8, 96, 129, 64, True),
+                                            (4, 100, 129, 64, False)])
 def test_graph_replay_prefill(B, H, T, d, causal):
     say(f"case prefill B={B} H={H} T={T} d={d} causal={causal}")
     q, k, v = (torch.empty(B, H, T, d, dtype=torch.bfloat16, device="cuda") for _ in range(3))

@@ -215,28 +215,37 @@ def test_prefill_bf16_shapes(B, H, Tq, Tkv, causal, d):
         assert attn.attn_last_kernel().startswith(f"prefill_bf16_d{d}<")
 
 
-# d = 64 has two kernels: 128-row tiles, and 64-row tiles whose key loop is
+# d = 64 has three kernels: 128-row tiles; 64-row tiles whose key loop is
 # split over two waves ("key_halves") when the 128-row tiles would number
-# fewer than 768.  Both are exercised here with ragged ends and offsets; the
-# key-halves cases with 48 heads also take its balanced (snake) unit order,
-# one of them with a partial last round.
+# fewer than 768; and, for full attention, 256-row tiles of two 32-row
+# sub-tiles per wave ("rows_per_wave=64") when their 512 resident tiles need
+# fewer rounds than the 128-row kernel's 768.  All are exercised here with
+# ragged ends and offsets; the key-halves cases with 48 heads also take its
+# balanced (snake) unit order, one of them with a partial last round; the
+# 256-row cases cover the head-major tile order (400 heads), the plain one
+# (393 heads), T_q > T_kv and a partly empty last sub-tile (500 rows).
 D64_PATH_CASES = [
-    # B, H, Tq, Tkv, causal, key halves
-    (8, 96, 129, 129, True, False),
-    (8, 96, 100, 300, True, False),
-    (4, 192, 200, 200, False, False),
-    (4, 12, 1000, 1000, True, True),
-    (2, 24, 1100, 1300, True, True),
-    (3, 5, 333, 333, False, True),
-    (1, 1, 65, 65, True, True),
+    # B, H, Tq, Tkv, causal, key halves, 256-row tiles
+    (8, 96, 129, 129, True, False, False),
+    (8, 96, 100, 300, True, False, False),
+    (4, 192, 200, 200, False, False, False),
+    (4, 12, 1000, 1000, True, True, False),
+    (2, 24, 1100, 1300, True, True, False),
+    (3, 5, 333, 333, False, True, False),
+    (1, 1, 65, 65, True, True, False),
+    (4, 100, 129, 200, False, False, True),
+    (3, 131, 250, 77, False, False, True),
+    (1, 200, 500, 500, False, False, True),
 ]
 
 
-@pytest.mark.parametrize("B,H,Tq,Tkv,causal,halves", D64_PATH_CASES)
-def test_prefill_bf16_d64_paths(B, H, Tq, Tkv, causal, halves):
+@pytest.mark.parametrize("B,H,Tq,Tkv,causal,halves,rows256", D64_PATH_CASES)
+def test_prefill_bf16_d64_paths(B, H, Tq, Tkv, causal, halves, rows256):
     full_check(Workload(f"bf16[{B},{H},{Tq},{Tkv},{'c' if causal else 'n'},d=64]", B, H, Tq, Tkv, 64, "bf16",
                         causal, seed=3 + B * H + Tq))
-    assert ("key_halves=2" in attn.attn_last_kernel()) == halves
+    kern = attn.attn_last_kernel()
+    assert ("key_halves=2" in kern) == halves, kern
+    assert ("rows_per_wave=64" in kern) == rows256, kern
 
 
 @pytest.mark.parametrize("d", [16, 32, 64, 128])
