@@ -116,6 +116,7 @@ PREFILL = [  # B, H, Tq, Tkv, d, causal -- small grids take the key-halves kerne
     (1, 4, 129, 700, 64, False),
     (1, 96, 1024, 1024, 64, True),      # 768 tiles of 128 rows: the 128-row kernel
     (1, 96, 1024, 1024, 64, False),
+    (4, 100, 129, 200, 64, False),      # 800 tiles of 128 rows, 400 of 256: the 256-row kernel
     (1, 4, 300, 300, 128, False),
     (2, 4, 1000, 1000, 128, True),
     (1, 4, 70, 513, 128, True),
