@@ -332,6 +332,8 @@ def test_fp32_scores_spread():
     (2, 3, 1000, 128, 16), (3, 2, 77, 64, 3), (1, 1, 1, 128, 16), (4, 4, 8192, 64, 16),
     (2, 2, 512, 128, 1), (2, 2, 513, 128, 2), (1, 2, 40, 128, 45), (5, 3, 4097, 128, 7),
     (1, 12, 16384, 64, 0), (1, 32, 1000, 128, 0), (1, 2, 5000, 64, 64), (1, 1, 20000, 128, 129),
+    (1, 4, 3000, 128, 0),       # automatic: 23 partitions (the minimum-keys cut of one per CU)
+    (1, 8, 16384, 64, 0),       # automatic: 32 partitions, one workgroup per CU
 ])
 def test_decode_shapes(B, H, Tkv, d, splits):
     full_check(Workload(f"decode[{B},{H},{Tkv},d={d},P={splits}]", B, H, 1, Tkv, d, "bf16", False,
