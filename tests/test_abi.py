@@ -219,9 +219,10 @@ def test_split_forward_workspace_formula():
 
 
 def test_decode_automatic_splits():
-    # 12 heads of one sequence: 512 workgroups would need 43 partitions; capped at 16
-    # (8-wave workgroups), then halved until partitions hold >= 64 KiB of K+V (256 keys
-    # at d=64, 128 at d=128)
+    # 12 heads of one sequence: doubling toward 512 workgroups stops at the cap of 16
+    # (8-wave workgroups), which leaves 192 of 256 CUs busy, so the grid takes
+    # 256 // 12 = 21 partitions (one workgroup per CU); no partition may hold less
+    # than 64 KiB of K+V (256 keys at d=64, 128 at d=128)
     assert attn.attn_decode_splits(1, 12, 12, 16384, 64) == 21   # 12 workgroups: one per CU
     assert attn.attn_decode_splits(1, 8, 8, 16384, 64) == 32
     assert attn.attn_decode_splits(1, 4, 4, 32768, 128) == 64
@@ -247,6 +248,28 @@ def test_decode_automatic_splits():
     assert attn.attn_decode_splits(1, 12, 5, 1024, 64) == 0
     assert attn.attn_decode_splits(1, 12, 12, 1024, 96) == 0
     assert attn.attn_decode_splits(0, 12, 12, 1024, 64) == 0
+
+
+def test_decode_automatic_splits_properties():
+    """Over batch, heads, groups, lengths and head widths: 1 <= P <= 64; the VALU
+    kernel (groups below 4) exceeds 16 partitions only on grids of fewer than 16
+    head tiles, and then keeps to one workgroup per CU; no partition holds fewer
+    than 16384 / d keys unless the cache itself is shorter; a grid below one
+    workgroup per CU gets at least 16 partitions when the keys allow it."""
+    for d in (64, 128):
+        min_keys = 16384 // d
+        for B in (1, 2, 3, 8, 64):
+            for Hkv, G in ((1, 1), (4, 1), (12, 1), (32, 1), (8, 2), (4, 4), (2, 8), (1, 32)):
+                Hq = Hkv * G
+                for T in (1, 100, 255, 256, 1000, 3000, 16384, 100000):
+                    p = attn.attn_decode_splits(B, Hq, Hkv, T, d)
+                    assert 1 <= p <= 64, (B, Hq, Hkv, T, d, p)
+                    assert p == 1 or T // p >= min_keys, (B, Hq, Hkv, T, d, p)
+                    if G < 4:
+                        tiles = B * Hkv * (G // (2 if G == 2 else 1))
+                        assert p <= 16 or tiles * p <= 256, (B, Hq, Hkv, T, d, p)
+                        if tiles < 16:
+                            assert p >= min(16, T // min_keys) or p == max(1, T // min_keys), (B, Hq, Hkv, T, d, p)
 
 
 def test_backward_arguments(lib):
