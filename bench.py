@@ -18,8 +18,10 @@ key axis split across workgroups, the split-KV decode step (64x32, 8192 keys,
 d=128, 16 partitions), its grouped-query form and a batch-1 decode step.
 
 Per leg: K timed steps (HIP events on the stream the kernels are launched on,
-bracketed by device synchronisation) after a clock-settling phase of
-back-to-back calls and W untimed warm-up steps; three repeats of at least
+bracketed by device synchronisation; for a leg whose K calls last under
+10 ms, as many calls as fill 10 ms, the count in its "steps") after a
+clock-settling phase of back-to-back calls and W untimed warm-up steps
+(the headline always times exactly K steps); three repeats of at least
 50 ms of back-to-back calls (per-call median and spread); the roofline
 fraction against the vendor peak, with the HBM bytes of committed rocprofv3
 counter summaries when they were taken on the current kernel sources; parity
@@ -208,6 +210,18 @@ def time_steps(torch, call, steps: int, warmup: int):
     return start.elapsed_time(end) / steps
 
 
+def time_leg(torch, call, steps: int, warmup: int, min_ms: float = 10.0):
+    """A leg's timed steps: the requested K steps, or, when K calls take less
+    than min_ms (where one late launch moves the mean), as many back-to-back
+    calls as fill min_ms.  Returns (ms per call, calls timed).  The headline
+    always times exactly K steps."""
+    ms = time_steps(torch, call, steps, warmup)
+    if ms * steps >= min_ms:
+        return ms, steps
+    n = math.ceil(min_ms / max(ms, 1e-4))
+    return time_steps(torch, call, n, 1), n
+
+
 def time_repeats(torch, call, ms_per_call: float, reps: int = 3, min_ms: float = 50.0):
     """Repeats of N back-to-back calls, N chosen so that each repeat lasts at
     least min_ms: the per-call time of each repeat, their median and spread
@@ -373,7 +387,7 @@ def workload_label(w, kind="prefill") -> str:
             f"{'causal' if w.causal else 'non-causal'} {w.dtype}")
 
 
-def run_prefill(torch, attn, name, args, cpu_seconds: float, cold: bool = False) -> dict:
+def run_prefill(torch, attn, name, args, cpu_seconds: float, cold: bool = False, headline: bool = False) -> dict:
     """One prefill workload: timing, repeats, roofline, parity, oracle leg and
     memory, all on the same inputs."""
     from io_aware_exact_amd.inputs import WORKLOADS, make_qkv
@@ -387,7 +401,10 @@ def run_prefill(torch, attn, name, args, cpu_seconds: float, cold: bool = False)
     f32 = w.dtype == "f32"
     call = attn.prepared_fwd(dq, dk, dv, o, lse, w.causal, w.scale, f32=f32)
     settled = settle(torch, call, args.settle_ms)
-    ms = time_steps(torch, call, args.steps, args.warmup)
+    if headline:
+        ms, nsteps = time_steps(torch, call, args.steps, args.warmup), args.steps
+    else:
+        ms, nsteps = time_leg(torch, call, args.steps, args.warmup)
     kern = attn.attn_last_kernel()
     reps = time_repeats(torch, call, ms)
     flops = prefill_flops(w)
@@ -405,7 +422,7 @@ def run_prefill(torch, attn, name, args, cpu_seconds: float, cold: bool = False)
         "value": tflops,
         "unit": "TFLOP/s",
         "ms_per_step": ms,
-        "steps": args.steps,
+        "steps": nsteps,
         "warmup": args.warmup,
         "settle_ms": settled,
         "kernel": kern,
@@ -468,7 +485,7 @@ def run_decode(torch, attn, name, args, cpu_seconds: float) -> dict:
                               device="cuda")
             ca = attn.prepared_decode(dq, dk, dv, o, lse, pa, wsa, w.scale)
             settle(torch, ca, args.settle_ms)
-            msa = time_steps(torch, ca, args.steps, args.warmup)
+            msa, _ = time_leg(torch, ca, args.steps, args.warmup)
             auto = {"splits": pa, "ms_per_step": msa, "value": total / (msa * 1e-3) / 1e9,
                     "kernel": attn.attn_last_kernel()}
             del wsa
@@ -477,11 +494,11 @@ def run_decode(torch, attn, name, args, cpu_seconds: float) -> dict:
         # pages measured at batch 1
         c1 = attn.prepared_decode(dq, dk, dv, o, lse, 1, None, w.scale)
         settle(torch, c1, args.settle_ms)
-        ms1 = time_steps(torch, c1, args.steps, args.warmup)
+        ms1, _ = time_leg(torch, c1, args.steps, args.warmup)
         unsplit = {"ms_per_step": ms1, "value": total / (ms1 * 1e-3) / 1e9, "kernel": attn.attn_last_kernel()}
     call = attn.prepared_decode(dq, dk, dv, o, lse, splits, ws, w.scale)
     settled = settle(torch, call, args.settle_ms)
-    ms = time_steps(torch, call, args.steps, args.warmup)
+    ms, nsteps = time_leg(torch, call, args.steps, args.warmup)
     kern = attn.attn_last_kernel()
     reps = time_repeats(torch, call, ms)
     gbps = total / (ms * 1e-3) / 1e9
@@ -523,7 +540,7 @@ def run_decode(torch, attn, name, args, cpu_seconds: float) -> dict:
         "unit": "GB/s",
         "kv_only_GBps": kv / (ms * 1e-3) / 1e9,
         "ms_per_step": ms,
-        "steps": args.steps,
+        "steps": nsteps,
         "warmup": args.warmup,
         "settle_ms": settled,
         "kernel": kern,
@@ -566,7 +583,7 @@ def run_backward(torch, attn, args, name="gpt2"):
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     call = attn.prepared_bwd(dq_, dk_, dv_, o, lse, ddo, gq, gk, gv, w.causal, ws, w.scale)
     settled = settle(torch, call, args.settle_ms)
-    ms = time_steps(torch, call, args.steps, args.warmup)
+    ms, nsteps = time_leg(torch, call, args.steps, args.warmup)
     kern = attn.attn_last_kernel()
     reps = time_repeats(torch, call, ms)
     mem = measure_memory(torch, call, lambda: attn.attn_bwd(dq_, dk_, dv_, o, lse, ddo, causal=w.causal,
@@ -590,7 +607,7 @@ def run_backward(torch, attn, args, name="gpt2"):
         "value": tf,
         "unit": "TFLOP/s",
         "ms_per_step": ms,
-        "steps": args.steps,
+        "steps": nsteps,
         "warmup": args.warmup,
         "settle_ms": settled,
         "kernel": kern,
@@ -620,14 +637,14 @@ def run_prefill_split(torch, attn, args, name="long_1head"):
     lse = torch.empty((w.B, w.H, w.Tq), dtype=torch.float32, device="cuda")
     cp = attn.prepared_fwd(dq, dk, dv, o, lse, w.causal, w.scale)
     settle(torch, cp, args.settle_ms)
-    ms_plain = time_steps(torch, cp, args.steps, args.warmup)
+    ms_plain, _ = time_leg(torch, cp, args.steps, args.warmup)
     kern_plain = attn.attn_last_kernel()
     o_plain = o.clone()
     nbytes = attn.attn_fwd_split_workspace_bytes(w.B, w.H, w.Tq, w.Tkv, w.d, w.causal, 0)
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
     call = attn.prepared_fwd(dq, dk, dv, o, lse, w.causal, w.scale, kv_chunk=0, workspace=ws)
     settled = settle(torch, call, args.settle_ms)
-    ms = time_steps(torch, call, args.steps, args.warmup)
+    ms, nsteps = time_leg(torch, call, args.steps, args.warmup)
     kern = attn.attn_last_kernel()
     reps = time_repeats(torch, call, ms)
     diff = float((o.float() - o_plain.float()).abs().max())
@@ -648,7 +665,7 @@ def run_prefill_split(torch, attn, args, name="long_1head"):
         "value": tf,
         "unit": "TFLOP/s",
         "ms_per_step": ms,
-        "steps": args.steps,
+        "steps": nsteps,
         "warmup": args.warmup,
         "settle_ms": settled,
         "kernel": kern,
@@ -909,7 +926,7 @@ def main():
         out["kernel_sources_digest"] = kernel_sources_digest()
         print(json.dumps(out), flush=True)
         return
-    head = run_prefill(torch, attn, args.workload, args, cpu_main, cold=True)
+    head = run_prefill(torch, attn, args.workload, args, cpu_main, cold=True, headline=True)
     props = torch.cuda.get_device_properties(0)
     result = {
         "metric": "attn fwd TFLOP/s (causal-adjusted) & % bf16 MFMA peak (prefill); decode KV GB/s & % HBM peak",
