@@ -424,22 +424,40 @@ def test_spread_scores_bf16():
     full_check(w.with_(causal=True, name="bf16_k3_causal"))
 
 
-def test_lse_optional_and_outputs_in_place():
-    w = Workload("inplace", 1, 2, 130, 130, 64, "bf16", True, seed=4)
+# one shape per forward kernel: key halves, 128-row causal, 256-row full
+# attention, head width 128, and a single query (the decode kernel)
+LSE_OPTIONAL_CASES = [
+    (1, 2, 130, 130, 64, True, "key_halves=2"),
+    (8, 96, 129, 129, 64, True, "bq=128"),
+    (4, 100, 129, 200, 64, False, "rows_per_wave=64"),
+    (1, 3, 200, 200, 128, False, "prefill_bf16_d128"),
+    (2, 3, 1, 300, 64, True, "decode_bf16"),
+]
+
+
+@pytest.mark.parametrize("B,H,Tq,Tkv,d,causal,kern", LSE_OPTIONAL_CASES)
+def test_lse_optional_and_outputs_in_place(B, H, Tq, Tkv, d, causal, kern):
+    """Without an LSE pointer the kernel writes O alone, bitwise equal to the
+    call that also writes the LSE, into the caller's buffer."""
+    w = Workload("inplace", B, H, Tq, Tkv, d, "bf16", causal, seed=4)
     q, k, v = [t.cuda() for t in make_qkv(w)]
-    o_ref, lse_ref = attn.attn_fwd(q, k, v, causal=True)
+    o_ref, lse_ref = attn.attn_fwd(q, k, v, causal=causal)
     out = torch.full_like(q, float("nan"))
-    o2 = attn.attn_fwd(q, k, v, causal=True, out=out, return_lse=False)
+    o2 = attn.attn_fwd(q, k, v, causal=causal, out=out, return_lse=False)
     torch.cuda.synchronize()
+    assert kern in attn.attn_last_kernel(), attn.attn_last_kernel()
     assert o2.data_ptr() == out.data_ptr()
     assert torch.equal(o2, o_ref)
 
 
-def test_deterministic_across_runs():
-    w = WORKLOADS["gpt2"].with_(B=1, H=4)
+@pytest.mark.parametrize("B,H,T,causal", [(1, 4, 1024, True), (4, 100, 129, False), (8, 96, 129, True)])
+def test_deterministic_across_runs(B, H, T, causal):
+    """Bitwise equal results from two calls (no atomics, no order that
+    depends on timing), on the key-halves, 256-row and 128-row kernels."""
+    w = WORKLOADS["gpt2"].with_(B=B, H=H, Tq=T, Tkv=T, causal=causal)
     q, k, v = [t.cuda() for t in make_qkv(w)]
-    o1, l1 = attn.attn_fwd(q, k, v, causal=True)
-    o2, l2 = attn.attn_fwd(q, k, v, causal=True)
+    o1, l1 = attn.attn_fwd(q, k, v, causal=causal)
+    o2, l2 = attn.attn_fwd(q, k, v, causal=causal)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
