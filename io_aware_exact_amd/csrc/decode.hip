@@ -425,7 +425,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                 const float p0 = fast_exp2(__builtin_fmaf(s[2 * i], c, -mref));
                 const float p1 = fast_exp2(__builtin_fmaf(s[2 * i + 1], c, -mref));
                 pw[i] = pack_bf16x2(p0, p1);
-                rs += p0 + p1;
+                rs = i == 0 ? p0 + p1 : rs + (p0 + p1);   // no add of the zero start value
             }
         };
         exponentiate(m);

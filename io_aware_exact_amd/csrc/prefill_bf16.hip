@@ -379,7 +379,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
                 const float p0 = fast_exp2(__builtin_fmaf(s[kt][r], c, -mref));
                 const float p1 = fast_exp2(__builtin_fmaf(s[kt][r + 1], c, -mref));
                 pw[i] = pack_bf16x2(p0, p1);
-                rs += p0 + p1;
+                rs = i == 0 ? p0 + p1 : rs + (p0 + p1);   // no add of the zero start value
             }
         };
         exponentiate(m);
@@ -472,7 +472,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
                 const float p0 = fast_exp2(__builtin_fmaf(s[kt][r], c, -mref));
                 const float p1 = fast_exp2(__builtin_fmaf(s[kt][r + 1], c, -mref));
                 pw[i] = pack_bf16x2(p0, p1);
-                rs += p0 + p1;
+                rs = i == 0 ? p0 + p1 : rs + (p0 + p1);   // no add of the zero start value
             }
         };
         exponentiate(m);
@@ -971,7 +971,7 @@ void prefill_bf16_d64_r256_kernel(const uint16_t* __restrict__ Q, const uint16_t
                     const float p0 = fast_exp2(__builtin_fmaf(s[u][kt][r], c, -mref));
                     const float p1 = fast_exp2(__builtin_fmaf(s[u][kt][r + 1], c, -mref));
                     pw[u][i] = pack_bf16x2(p0, p1);
-                    rs += p0 + p1;
+                    rs = i == 0 ? p0 + p1 : rs + (p0 + p1);   // no add of the zero start value
                 }
             };
             exponentiate(m[u]);
