@@ -288,10 +288,11 @@ void decode_combine_kernel(const float* __restrict__ part, uint16_t* __restrict_
 // partition): the wave streams its partition's K/V blocks through a private
 // NS-stage LDS ring by non-temporal DMA (no barriers), K read as rows, V with
 // ds_read_b64_tr_b16.  The reference max is raised lazily as in prefill (when
-// a head's block sum would exceed 2^16 or is not finite).  Partial records
+// either lane's half of a head's block sum would exceed 2^15, so the block
+// sum stays within 2^16, or is not finite).  Partial records
 // and the combine kernel are those of the VALU kernel.
 constexpr int MF_BLK = 32;   // keys per block
-constexpr float kMfSumLimit = 65536.0f;
+constexpr float kMfHalfSumLimit = 32768.0f;   // per lane: half of a head's keys
 
 template <int D>
 struct MfGeo;
@@ -429,7 +430,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
             }
         };
         exponentiate(m);
-        if (__builtin_amdgcn_ballot_w64(!(half_swap_sum(rs) <= kMfSumLimit)) != 0) {
+        if (__builtin_amdgcn_ballot_w64(!(rs <= kMfHalfSumLimit)) != 0) {
             float mx = kNegInf;
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);

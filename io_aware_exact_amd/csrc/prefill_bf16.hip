@@ -20,12 +20,13 @@
 // otherwise produce large terms.  The final O / l and m + log2 l do not depend
 // on which reference was used (the rescaling factors telescope), so any m not
 // far below the running maximum gives the exact result; m is raised (and l, O
-// rescaled by exp2(m_old - m_new)) whenever a row's block sum exceeds 2^16 or
-// is not finite, which bounds every term by 2^16 and keeps fp32 far from
-// overflow.  Blocks therefore cost no row-max in the common case: softmax work
-// is one FMA, one exp2 and one add per score and a bf16 pack per pair -- the
-// VALU budget is what limits a d = 64 head on CDNA4, since each score carries
-// only 4*64 MFMA flops.  (The row sum stays fp32: a sum of the bf16-rounded
+// rescaled by exp2(m_old - m_new)) whenever either half of a row's block sum
+// (the keys one lane holds) exceeds 2^15 or is not finite, which bounds every
+// block row sum by 2^16 and keeps fp32 far from overflow.  Blocks therefore
+// cost no row max and no exchange between lanes in the common case: softmax
+// work is one FMA, one exp2 and one add per score and a bf16 pack per pair --
+// the VALU budget is what limits a d = 64 head on CDNA4, since each score
+// carries only 4*64 MFMA flops.  (The row sum stays fp32: a sum of the bf16-rounded
 // terms would cost the log-sum-exp up to 2^-9 relative on short rows.)
 //
 // Layout choices for CDNA4:
@@ -63,7 +64,11 @@
 namespace attn {
 namespace {
 
-constexpr float kSumLimit = 65536.0f;         // 2^16: largest block row sum kept without raising m
+// Largest share of a block row sum that one lane (half of the row's keys)
+// keeps without raising m: 2^15, so the row's block sum stays within 2^16.
+// Each lane tests its own half, and the test needs no exchange between the
+// two halves.
+constexpr float kHalfSumLimit = 32768.0f;
 
 // A 16-byte LDS load at an LDS byte address plus a constant (the constant
 // lands in the instruction's offset field); the compiler tracks its wait.
@@ -383,8 +388,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
             }
         };
         exponentiate(m);
-        const float row = half_swap_sum(rs);
-        if (__builtin_amdgcn_ballot_w64(!(row <= kSumLimit)) != 0) {
+        if (__builtin_amdgcn_ballot_w64(!(rs <= kHalfSumLimit)) != 0) {
             // raise the reference to the true running max and rescale
             float mx = kNegInf;
 #pragma unroll
@@ -476,8 +480,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
             }
         };
         exponentiate(m);
-        const float row = half_swap_sum(rs);
-        if (__builtin_amdgcn_ballot_w64(!(row <= kSumLimit)) != 0) {
+        if (__builtin_amdgcn_ballot_w64(!(rs <= kHalfSumLimit)) != 0) {
             // raise the reference to the true running max and rescale
             float mx = kNegInf;
 #pragma unroll
@@ -625,8 +628,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
                 }
             };
             exponentiate(m);
-            const float row = half_swap_sum(rs);
-            if (__builtin_amdgcn_ballot_w64(!(row <= kSumLimit)) != 0) {
+            if (__builtin_amdgcn_ballot_w64(!(rs <= kHalfSumLimit)) != 0) {
                 float mx = kNegInf;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
@@ -975,8 +977,7 @@ void prefill_bf16_d64_r256_kernel(const uint16_t* __restrict__ Q, const uint16_t
                 }
             };
             exponentiate(m[u]);
-            const float row = half_swap_sum(rs);
-            if (__builtin_amdgcn_ballot_w64(!(row <= kSumLimit)) != 0) {
+            if (__builtin_amdgcn_ballot_w64(!(rs <= kHalfSumLimit)) != 0) {
                 // raise the reference to the true running max and rescale
                 float mx = kNegInf;
 #pragma unroll
