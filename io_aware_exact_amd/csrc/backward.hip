@@ -185,11 +185,6 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     // query blocks that see any key of this tile (bottom-right causal)
     const int nqb = (Tq + BQ2 - 1) / BQ2;
     const int qb_first = CAUSAL ? max(0, k0 - off) / BQ2 : 0;
-    // blocks from qb_free on are visible to every key of the tile and full
-    const int tile_last_key = min(k0 + BKVT, Tkv) - 1;
-    int qb_free = CAUSAL ? (max(0, tile_last_key - off) + BQ2 - 1) / BQ2 : 0;
-    qb_free = max(qb_free, qb_first);
-    const int qb_full_end = Tq / BQ2;             // blocks before this have no ragged rows
 
     // DMA: wave w moves row groups g = w + 4i (1 KiB) of Q and dO, and every
     // wave moves the block's row statistics (BQ2 * 8 bytes)
@@ -239,8 +234,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         }
 
     // one 32-row sub-tile qs of the block staged at `st`; q0 = first row of the block
-    auto subtile = [&](const uint8_t* st, int q0, int qs, auto mask_tag) {
-        constexpr bool MASK = decltype(mask_tag)::value;
+    auto subtile = [&](const uint8_t* st, int q0, int qs) {
         const uint8_t* qst = st;
         const uint8_t* gst = st + QBLK;
         const float* sst = reinterpret_cast<const float*>(st + 2 * QBLK);
@@ -270,12 +264,11 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                 const float lse2 = (i < 2) ? st0[2 * i] : st1[2 * (i - 2)];
                 const float dd = (i < 2) ? st0[2 * i + 1] : st1[2 * (i - 2) + 1];
                 const int r = 4 * g4 + i;
+                // a masked score (a row past Tq, or causal and right of the
+                // diagonal) gets exponent -inf: exp2 gives 0, no branch
+                const int qrow = q0 + rb + i;
                 float x = __builtin_fmaf(s[r], c, -lse2);
-                if constexpr (MASK) {
-                    // a masked score gets exponent -inf: exp2 gives 0, no branch
-                    const int qrow = q0 + rb + i;
-                    x = (qrow >= Tq || (CAUSAL && key > qrow + off)) ? -__builtin_inff() : x;
-                }
+                x = (qrow >= Tq || (CAUSAL && key > qrow + off)) ? -__builtin_inff() : x;
                 const float pe = fast_exp2(x);
                 p[i] = pe;
                 ds[i] = pe * (dp[r] - dd);
@@ -333,16 +326,18 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         issue(j + NS - 1);
         const uint8_t* st = &ring[j % NS][0];
         const int q0 = j * BQ2;
-        const bool free_blk = (j >= qb_free) && (j < qb_full_end);
-        // one sub-tile at a time (not unrolled: two would double the live registers)
+        // Every sub-tile runs the one body with the element mask, also where
+        // no element is masked or where every element is (a wave whose keys
+        // follow all of a sub-tile's rows then adds exact zeros).  A branch
+        // between an unmasked and a masked body, or around the body, makes
+        // the register allocator copy the four accumulators (64 VGPRs) at
+        // the join in every iteration.
+        if constexpr (QS == 2) {
+            subtile(st, q0, qh);
+        } else {
+            // one sub-tile at a time (not unrolled: two would double the live registers)
 #pragma nounroll
-        for (int qs = QS == 2 ? qh : 0; qs < NSUB; qs += QS) {
-            if (free_blk) {
-                subtile(st, q0, qs, std::false_type{});
-            } else if (!CAUSAL || q0 + 32 * qs + 31 + off >= k0 + 32 * kg) {
-                // a wave whose keys all lie right of every row of a sub-tile skips it
-                subtile(st, q0, qs, std::true_type{});
-            }
+            for (int qs = 0; qs < NSUB; ++qs) subtile(st, q0, qs);
         }
     }
     wait_vmcnt<0>();    // no DMA may still be writing LDS when the workgroup retires
