@@ -264,11 +264,13 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                 const float lse2 = (i < 2) ? st0[2 * i] : st1[2 * (i - 2)];
                 const float dd = (i < 2) ? st0[2 * i + 1] : st1[2 * (i - 2) + 1];
                 const int r = 4 * g4 + i;
-                // a masked score (a row past Tq, or causal and right of the
-                // diagonal) gets exponent -inf: exp2 gives 0, no branch
-                const int qrow = q0 + rb + i;
+                // causal: a key right of the row's diagonal gets exponent
+                // -inf (exp2 gives 0, no branch).  Rows past Tq need no mask:
+                // their Q, dO and statistics arrive zero-filled, so p = 1,
+                // dS = p (0 - 0) = 0 and the dO^T column is 0 -- they add
+                // exact zeros to dV and dK.
                 float x = __builtin_fmaf(s[r], c, -lse2);
-                x = (qrow >= Tq || (CAUSAL && key > qrow + off)) ? -__builtin_inff() : x;
+                if constexpr (CAUSAL) x = key > q0 + rb + i + off ? -__builtin_inff() : x;
                 const float pe = fast_exp2(x);
                 p[i] = pe;
                 ds[i] = pe * (dp[r] - dd);
@@ -326,9 +328,9 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         issue(j + NS - 1);
         const uint8_t* st = &ring[j % NS][0];
         const int q0 = j * BQ2;
-        // Every sub-tile runs the one body with the element mask, also where
-        // no element is masked or where every element is (a wave whose keys
-        // follow all of a sub-tile's rows then adds exact zeros).  A branch
+        // Every sub-tile runs the one body with the causal element mask, also
+        // where no element is masked or where every element is (a wave whose
+        // keys follow all of a sub-tile's rows then adds exact zeros).  A branch
         // between an unmasked and a masked body, or around the body, makes
         // the register allocator copy the four accumulators (64 VGPRs) at
         // the join in every iteration.
