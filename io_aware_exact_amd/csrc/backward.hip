@@ -68,34 +68,12 @@ __device__ __forceinline__ uint32_t tr_off(int row, int col) {
     return (uint32_t)(row * D * 2 + ((((col >> 3) ^ BwdGeo<D>::swz(row)) << 4) | ((col & 4) << 1)));
 }
 
-// Transposed reads for the 16-row k-step STP of a 32-row group at byte
-// `base`: every 32-column tile, rows 16 STP + (0..7) and + 8.  Rows r and
-// r + 8 differ in their swizzle, rows r and r + 16 do not, so each tile keeps
-// one offset per 8-row half and the k-step is an immediate.
-template <int D, int STP>
-__device__ __forceinline__ void tr_kstep(uint32_t base, const uint32_t (&o)[D / 32][2], u32x4_t (&a)[D / 32]) {
-    constexpr int OFF = STP * 16 * D * 2;
-#pragma unroll
-    for (int d2 = 0; d2 < D / 32; d2 += 2)
-        lds_read_tr16_x4<OFF, OFF, OFF, OFF>(base + o[d2][0], base + o[d2][1], base + o[d2 + 1][0],
-                                             base + o[d2 + 1][1], a[d2], a[d2 + 1]);
-}
-
-// Head width 64: the transposed operands of two k-steps at once (k-step S0 of
-// the 32-row group at `base0`, k-step S1 of the group at `base1`) behind one
-// wait.
-template <int S0, int S1>
-__device__ __forceinline__ void tr_kstep2_d64(uint32_t base0, uint32_t base1, const uint32_t (&o)[2][2],
-                                              u32x4_t (&a0)[2], u32x4_t (&a1)[2]) {
-    constexpr int F0 = S0 * 16 * 64 * 2, F1 = S1 * 16 * 64 * 2;
-    const uint32_t ad[8] = {base0 + o[0][0], base0 + o[0][1], base0 + o[1][0], base0 + o[1][1],
-                            base1 + o[0][0], base1 + o[0][1], base1 + o[1][0], base1 + o[1][1]};
-    u32x4_t r[4];
-    lds_read_tr16_x8<F0, F0, F0, F0, F1, F1, F1, F1>(ad, r);
-    a0[0] = r[0];
-    a0[1] = r[1];
-    a1[0] = r[2];
-    a1[1] = r[3];
+// 16-byte LDS load at a byte address plus a constant (the instruction's
+// offset field); the compiler tracks its wait.
+template <int OFF>
+__device__ __forceinline__ bf16x8_t lds_b128(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "16-bit LDS instruction offset");
+    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>((uintptr_t)(addr + OFF));
 }
 
 // Transposed-read offsets of a lane: lane group lg = lane / 16, jj = lane % 16
@@ -110,6 +88,53 @@ __device__ __forceinline__ void tr_offsets(int lane, uint32_t (&o)[D / 32][2]) {
         o[dt][0] = tr_off<D>(row, col);
         o[dt][1] = tr_off<D>(row + 8, col);
     }
+}
+
+// Transposed reads for the 16-row k-step STP of a 32-row group: every
+// 32-column tile dt, rows 16 STP + (0..7) and + 8, at the lane's addresses
+// a[dt][0] and a[dt][1] (ring base and tr_offsets) plus a constant OFF (ring
+// stage and operand).  Rows r and r + 8 differ in their swizzle, rows r and
+// r + 16 do not, so each tile keeps one address per 8-row half and the
+// k-step is an immediate.
+template <int D, int STP, int OFF>
+__device__ __forceinline__ void tr_kstep_at(const uint32_t (&a)[D / 32][2], u32x4_t (&r)[D / 32]) {
+    constexpr int F = OFF + STP * 16 * D * 2;
+#pragma unroll
+    for (int d2 = 0; d2 < D / 32; d2 += 2)
+        lds_read_tr16_x4<F, F, F, F>(a[d2][0], a[d2][1], a[d2 + 1][0], a[d2 + 1][1], r[d2], r[d2 + 1]);
+}
+
+// Head width 64: k-steps S0 and S1 of one operand behind one wait.
+template <int S0, int S1, int OFF>
+__device__ __forceinline__ void tr_kstep2_d64_at(const uint32_t (&a)[2][2], u32x4_t (&r0)[2], u32x4_t (&r1)[2]) {
+    constexpr int F0 = OFF + S0 * 16 * 64 * 2, F1 = OFF + S1 * 16 * 64 * 2;
+    const uint32_t ad[8] = {a[0][0], a[0][1], a[1][0], a[1][1], a[0][0], a[0][1], a[1][0], a[1][1]};
+    u32x4_t r[4];
+    lds_read_tr16_x8<F0, F0, F0, F0, F1, F1, F1, F1>(ad, r);
+    r0[0] = r[0];
+    r0[1] = r[1];
+    r1[0] = r[2];
+    r1[1] = r[3];
+}
+
+// Head width 64: k-step STP of two operands at constants G and Q from the
+// same addresses (dO and Q, one block apart in a stage) behind one wait.
+template <int STP, int G, int Q>
+__device__ __forceinline__ void tr_kstep2_d64_pair_at(const uint32_t (&a)[2][2], u32x4_t (&rg)[2],
+                                                      u32x4_t (&rq)[2]) {
+    constexpr int F0 = G + STP * 16 * 64 * 2, F1 = Q + STP * 16 * 64 * 2;
+    const uint32_t ad[8] = {a[0][0], a[0][1], a[1][0], a[1][1], a[0][0], a[0][1], a[1][0], a[1][1]};
+    u32x4_t r[4];
+    lds_read_tr16_x8<F0, F0, F0, F0, F1, F1, F1, F1>(ad, r);
+    rg[0] = r[0];
+    rg[1] = r[1];
+    rq[0] = r[2];
+    rq[1] = r[3];
+}
+
+// 16-byte LDS load of four floats at a byte address plus a byte offset.
+__device__ __forceinline__ f32x4_t lds_f32x4(uint32_t addr, int off) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>((uintptr_t)(addr + off));
 }
 
 // ------------------------------------------------------------------ dK, dV
@@ -204,7 +229,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         const __amdgpu_buffer_rsrc_t rg = make_rsrc(dO + qbase + eoff, bytes);
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(stats + (size_t)bh * Tq + (live ? q0 : 0),
                                                     live ? (uint32_t)(Tq - q0) * 8u : 0u);
-        uint8_t* st = &ring[j % NS][0];
+        uint8_t* st = &ring[(j - qb_first) % NS][0];   // block j sits in stage (j - qb_first) % NS
 #pragma unroll
         for (int i = 0; i < KV_LI; ++i) {
             const int g = wave + KV_WAVES * i;
@@ -233,11 +258,27 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
             dvt[dt][r] = 0.f;
         }
 
-    // one 32-row sub-tile qs of the block staged at `st`; q0 = first row of the block
-    auto subtile = [&](const uint8_t* st, int q0, int qs) {
-        const uint8_t* qst = st;
-        const uint8_t* gst = st + QBLK;
-        const float* sst = reinterpret_cast<const float*>(st + 2 * QBLK);
+    // Per-lane LDS addresses in ring stage 0 (query halves: of this wave's
+    // sub-tile); a stage adds a constant, so the block loop below is unrolled
+    // by the ring depth and blocks need no address arithmetic.
+    const uint32_t ring_lds = lds_addr(&ring[0][0]);
+    const uint32_t sub0 = QS == 2 ? (uint32_t)(qh * 32 * ROWB) : 0u;
+    uint32_t q_ra[TQ];                   // rows of Q (dO: + QBLK)
+#pragma unroll
+    for (int t = 0; t < TQ; ++t) q_ra[t] = ring_lds + sub0 + r_off[t];
+    uint32_t t_ra[DT][2];                // transposed reads of Q (dO: + QBLK)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        t_ra[dt][0] = ring_lds + sub0 + t_off[dt][0];
+        t_ra[dt][1] = ring_lds + sub0 + t_off[dt][1];
+    }
+    // row statistics (lse2, D) of rows 4hf.. of the sub-tile
+    const uint32_t s_ra = ring_lds + 2 * QBLK + (uint32_t)((QS == 2 ? qh * 32 : 0) * 8 + 4 * hf * 8);
+
+    // one 32-row sub-tile of the block in ring stage S; q0 = first row of the
+    // block, qs = the sub-tile, qo = its byte offset beyond the addresses above
+    auto subtile = [&](auto stage_tag, int q0, int qs, uint32_t qo, uint32_t so8) {
+        constexpr int SO = decltype(stage_tag)::value * STAGE;
         f32x16_t s, dp;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -246,8 +287,8 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         }
 #pragma unroll
         for (int t = 0; t < TQ; ++t) {
-            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(qst + r_off[t] + qs * 32 * ROWB);
-            const bf16x8_t g = *reinterpret_cast<const bf16x8_t*>(gst + r_off[t] + qs * 32 * ROWB);
+            const bf16x8_t a = lds_b128<SO>(q_ra[t] + qo);
+            const bf16x8_t g = lds_b128<SO + QBLK>(q_ra[t] + qo);
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[t], s, 0, 0, 0);
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(g, vf[t], dp, 0, 0, 0);
         }
@@ -256,8 +297,8 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
             const int rb = qs * 32 + 8 * g4 + 4 * hf;           // first of 4 consecutive rows
-            const f32x4_t st0 = *reinterpret_cast<const f32x4_t*>(sst + 2 * rb);      // (lse2, D) rows rb, rb+1
-            const f32x4_t st1 = *reinterpret_cast<const f32x4_t*>(sst + 2 * rb + 4);  // rows rb+2, rb+3
+            const f32x4_t st0 = lds_f32x4(s_ra + so8, SO + 64 * g4);       // (lse2, D) rows rb, rb+1
+            const f32x4_t st1 = lds_f32x4(s_ra + so8, SO + 64 * g4 + 16);  // rows rb+2, rb+3
             float p[4], ds[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -281,8 +322,12 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
             dw[2 * g4 + 1] = pack_bf16x2(ds[2], ds[3]);
         }
         // dV^T += dO^T P and dK^T += Q^T dS over the sub-tile's 32 rows (two 16-row k-steps)
-        const uint32_t gb = lds_addr(gst) + qs * 32 * ROWB;
-        const uint32_t qb = lds_addr(qst) + qs * 32 * ROWB;
+        uint32_t ta[DT][2];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            ta[dt][0] = t_ra[dt][0] + qo;
+            ta[dt][1] = t_ra[dt][1] + qo;
+        }
         auto kstep = [&](auto stp_tag) {
             constexpr int stp = decltype(stp_tag)::value;
             const u32x4_t pv = {pw[4 * stp], pw[4 * stp + 1], pw[4 * stp + 2], pw[4 * stp + 3]};
@@ -293,7 +338,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                 // dO^T and Q^T operands of this k-step behind one wait (the
                 // 8 extra registers would make QS = 1 spill)
                 u32x4_t ag[2], aq[2];
-                tr_kstep2_d64<stp, stp>(gb, qb, t_off, ag, aq);
+                tr_kstep2_d64_pair_at<stp, SO + QBLK, SO>(ta, ag, aq);
 #pragma unroll
                 for (int dt = 0; dt < 2; ++dt)
                     dvt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ag[dt]), pb,
@@ -304,12 +349,12 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                                                                       dkt[dt], 0, 0, 0);
             } else {
                 u32x4_t a[DT];
-                tr_kstep<D, stp>(gb, t_off, a);
+                tr_kstep_at<D, stp, SO + QBLK>(ta, a);
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt)
                     dvt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[dt]), pb,
                                                                       dvt[dt], 0, 0, 0);
-                tr_kstep<D, stp>(qb, t_off, a);
+                tr_kstep_at<D, stp, SO>(ta, a);
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt)
                     dkt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[dt]), db,
@@ -322,26 +367,36 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 
 #pragma unroll
     for (int j = 0; j < NS - 1; ++j) issue(qb_first + j);
-    for (int j = qb_first; j < nqb; ++j) {
+    // Every sub-tile runs the one body with the causal element mask, also
+    // where no element is masked or where every element is (a wave whose
+    // keys follow all of a sub-tile's rows then adds exact zeros).  A branch
+    // between an unmasked and a masked body, or around the body, makes the
+    // register allocator copy the four accumulators (64 VGPRs) at the join
+    // in every iteration.
+    auto blk = [&](int j, auto stage_tag) {
         wait_vmcnt<(2 * KV_LI + 1) * (NS - 2)>();   // this wave's part of block j has landed
-        __syncthreads();                            // ... everyone's, and stage (j-1) % NS is free
+        __syncthreads();                            // ... everyone's, and the previous stage is free
         issue(j + NS - 1);
-        const uint8_t* st = &ring[j % NS][0];
         const int q0 = j * BQ2;
-        // Every sub-tile runs the one body with the causal element mask, also
-        // where no element is masked or where every element is (a wave whose
-        // keys follow all of a sub-tile's rows then adds exact zeros).  A branch
-        // between an unmasked and a masked body, or around the body, makes
-        // the register allocator copy the four accumulators (64 VGPRs) at
-        // the join in every iteration.
+        __builtin_amdgcn_sched_barrier(0);          // no instruction moves between blocks
         if constexpr (QS == 2) {
-            subtile(st, q0, qh);
+            subtile(stage_tag, q0, qh, 0u, 0u);
         } else {
             // one sub-tile at a time (not unrolled: two would double the live registers)
 #pragma nounroll
-            for (int qs = 0; qs < NSUB; ++qs) subtile(st, q0, qs);
+            for (int qs = 0; qs < NSUB; ++qs)
+                subtile(stage_tag, q0, qs, (uint32_t)(qs * 32 * ROWB), (uint32_t)(qs * 32 * 8));
         }
+    };
+    static_assert(NS == 3, "the unrolled loop below assumes a 3-stage ring");
+    int j = qb_first;
+    for (; j + 2 < nqb; j += 3) {
+        blk(j, std::integral_constant<int, 0>{});
+        blk(j + 1, std::integral_constant<int, 1>{});
+        blk(j + 2, std::integral_constant<int, 2>{});
     }
+    if (j < nqb) blk(j, std::integral_constant<int, 0>{});
+    if (j + 1 < nqb) blk(j + 1, std::integral_constant<int, 1>{});
     wait_vmcnt<0>();    // no DMA may still be writing LDS when the workgroup retires
 
     if constexpr (QS == 2) {
@@ -404,8 +459,10 @@ constexpr int BQ = 32 * DQ_WAVES;   // query rows per workgroup
 // 32-key halves of every key block; the pair sums its dQ partials through LDS
 // at the end.  Tiles are then 64 rows and the serial key loop of a tile is
 // half as long.
+// Three waves per SIMD at d = 64 (the one-row-group form then spills four
+// registers and is still faster than at two waves).
 template <int D, bool CAUSAL, int KS = 1>
-__global__ __launch_bounds__(DQ_WAVES * 64, 2)
+__global__ __launch_bounds__(DQ_WAVES * 64, D == 64 ? 3 : 2)
 void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                    const uint16_t* __restrict__ O, const float* __restrict__ LSE,
@@ -519,10 +576,25 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 #pragma unroll
         for (int r = 0; r < 16; ++r) dqt[dt][r] = 0.f;
 
-    // one block for this wave: its WKT 32-key tiles start at kst (kb = first key)
-    auto step = [&](const uint8_t* kst, int kb, auto mask_tag) {
+    // Per-lane LDS addresses in ring stage 0 of this wave's keys (rows
+    // wko.. of the stage); a stage adds a constant, so the loop below is
+    // unrolled by the ring depth and blocks need no address arithmetic.
+    const int wko = KS == 2 ? kh * 32 : 0;
+    const uint32_t ring0 = lds_addr(&ring[0][0][0]) + (uint32_t)(wko * ROWB);
+    uint32_t k_ra[TQ];
+#pragma unroll
+    for (int t = 0; t < TQ; ++t) k_ra[t] = ring0 + r_off[t];
+    uint32_t t_ra[DT][2];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        t_ra[dt][0] = ring0 + t_off[dt][0];
+        t_ra[dt][1] = ring0 + t_off[dt][1];
+    }
+
+    // one block for this wave in ring stage S: its WKT 32-key tiles (kb = first key)
+    auto step = [&](auto stage_tag, int kb, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
-        const uint8_t* vst = kst + KBLK;
+        constexpr int SO = decltype(stage_tag)::value * 2 * KBLK;
         // S^T and dP^T for the wave's keys; lane = query column
         uint32_t dw[8 * WKT];
 #pragma unroll
@@ -535,8 +607,8 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
             }
 #pragma unroll
             for (int t = 0; t < TQ; ++t) {
-                const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kst + r_off[t] + kt * 32 * ROWB);
-                const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(vst + r_off[t] + kt * 32 * ROWB);
+                const bf16x8_t a = kt ? lds_b128<SO + 32 * ROWB>(k_ra[t]) : lds_b128<SO>(k_ra[t]);
+                const bf16x8_t b = kt ? lds_b128<SO + KBLK + 32 * ROWB>(k_ra[t]) : lds_b128<SO + KBLK>(k_ra[t]);
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s, 0, 0, 0);
                 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, gf[t], dp, 0, 0, 0);
             }
@@ -555,13 +627,12 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
             for (int i = 0; i < 8; ++i) dw[8 * kt + i] = pack_bf16x2(ds[2 * i], ds[2 * i + 1]);
         }
         // dQ^T += K^T dS^T: four 16-key k-steps
-        const uint32_t kbase = lds_addr(kst);
         auto kstep = [&](auto stp_tag) {
             constexpr int stp = decltype(stp_tag)::value;
             const u32x4_t dv = {dw[4 * stp], dw[4 * stp + 1], dw[4 * stp + 2], dw[4 * stp + 3]};
             const bf16x8_t db = __builtin_bit_cast(bf16x8_t, dv);
             u32x4_t a[DT];
-            tr_kstep<D, stp>(kbase, t_off, a);
+            tr_kstep_at<D, stp, SO>(t_ra, a);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
                 dqt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[dt]), db, dqt[dt],
@@ -571,7 +642,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         auto kstep_pair = [&](auto stp_tag) {
             constexpr int stp = decltype(stp_tag)::value;
             u32x4_t a0[2], a1[2];
-            tr_kstep2_d64<stp, stp + 1>(kbase, kbase, t_off, a0, a1);
+            tr_kstep2_d64_at<stp, stp + 1, SO>(t_ra, a0, a1);
             const u32x4_t d0 = {dw[4 * stp], dw[4 * stp + 1], dw[4 * stp + 2], dw[4 * stp + 3]};
             const u32x4_t d1 = {dw[4 * stp + 4], dw[4 * stp + 5], dw[4 * stp + 6], dw[4 * stp + 7]};
 #pragma unroll
@@ -599,22 +670,33 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     const int nfull = CAUSAL ? min(Tkv / BK, (q0 + off + 1) / BK) : Tkv / BK;
 #pragma unroll
     for (int j = 0; j < NS - 1; ++j) issue(j);
-    // this wave's keys of a block: rows [kh * 32 * WKT, ...) of the stage
-    const int wko = KS == 2 ? kh * 32 : 0;
-    int j = 0;
-    for (; j < nfull; ++j) {
-        wait_vmcnt<2 * DQ_LI * (NS - 2)>();
-        __syncthreads();
-        issue(j + NS - 1);
-        step(&ring[j % NS][0][0] + wko * ROWB, j * BK + wko, std::false_type{});
-    }
-    for (; j < nblk; ++j) {
+    static_assert(NS == 3, "the unrolled loop below assumes a 3-stage ring");
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    // block j sits in stage j % NS
+    auto blk = [&](int j, auto stage_tag, auto mask_tag) {
         wait_vmcnt<2 * DQ_LI * (NS - 2)>();
         __syncthreads();
         issue(j + NS - 1);
         const int kb = j * BK + wko;
-        if (!CAUSAL || kb <= wq_last + off) step(&ring[j % NS][0][0] + wko * ROWB, kb, std::true_type{});
+        if (!decltype(mask_tag)::value || !CAUSAL || kb <= wq_last + off) step(stage_tag, kb, mask_tag);
+    };
+    auto blk_any = [&](int j, auto mask_tag) {
+        switch (j % NS) {
+            case 0: blk(j, I0{}, mask_tag); break;
+            case 1: blk(j, I1{}, mask_tag); break;
+            default: blk(j, I2{}, mask_tag); break;
+        }
+    };
+    int j = 0;
+    for (; j + 2 < nfull; j += 3) {
+        blk(j, I0{}, std::false_type{});
+        blk(j + 1, I1{}, std::false_type{});
+        blk(j + 2, I2{}, std::false_type{});
     }
+    for (; j < nfull; ++j) blk_any(j, std::false_type{});
+    for (; j < nblk; ++j) blk_any(j, std::true_type{});
     wait_vmcnt<0>();
 
     if constexpr (KS == 2) {
