@@ -538,7 +538,6 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 
     const int kend = CAUSAL ? min(Tkv, q0 + BQT + off) : Tkv;
     const int nblk = (kend + BK - 1) / BK;
-    const int wq_last = q0 + rg * 32 + 31;
     const int lim = CAUSAL ? min(Tkv - 1, qrow + off) : (Tkv - 1);   // last key this row sees
 
     uint32_t voff[DQ_LI];
@@ -679,15 +678,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         wait_vmcnt<2 * DQ_LI * (NS - 2)>();
         __syncthreads();
         issue(j + NS - 1);
-        const int kb = j * BK + wko;
-        if (!decltype(mask_tag)::value || !CAUSAL || kb <= wq_last + off) step(stage_tag, kb, mask_tag);
-    };
-    auto blk_any = [&](int j, auto mask_tag) {
-        switch (j % NS) {
-            case 0: blk(j, I0{}, mask_tag); break;
-            case 1: blk(j, I1{}, mask_tag); break;
-            default: blk(j, I2{}, mask_tag); break;
-        }
+        step(stage_tag, j * BK + wko, mask_tag);
     };
     int j = 0;
     for (; j + 2 < nfull; j += 3) {
@@ -695,8 +686,19 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         blk(j + 1, I1{}, std::false_type{});
         blk(j + 2, I2{}, std::false_type{});
     }
-    for (; j < nfull; ++j) blk_any(j, std::false_type{});
-    for (; j < nblk; ++j) blk_any(j, std::true_type{});
+    // The rest (at most two unmasked blocks, then the diagonal and ragged
+    // ones) runs the masked body, also for a block whose keys all follow this
+    // wave's rows (every score masked: it adds exact zeros), three blocks at
+    // a time from j = 0 mod 3, so stages stay compile-time.  A stage chosen
+    // at run time, or a branch around a block, made the register allocator
+    // copy the accumulator at the join on every such block.
+    for (; j + 2 < nblk; j += 3) {
+        blk(j, I0{}, std::true_type{});
+        blk(j + 1, I1{}, std::true_type{});
+        blk(j + 2, I2{}, std::true_type{});
+    }
+    if (j < nblk) blk(j, I0{}, std::true_type{});
+    if (j + 1 < nblk) blk(j + 1, I1{}, std::true_type{});
     wait_vmcnt<0>();
 
     if constexpr (KS == 2) {

@@ -656,11 +656,6 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
                 }
             }
         };
-        // a block whose stage is known only at run time
-        auto body_any = [&](int j, f32x16_t& sc, f32x16_t& nxt, auto mask_tag) {
-            if (j & 1) body(j, sc, nxt, mask_tag, I1{});
-            else body(j, sc, nxt, mask_tag, I0{});
-        };
         f32x16_t sa = qk(I0{}), sb;
         int j = 0;
         const int jfull = min(nfull, jhi);
@@ -677,14 +672,18 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
             body(j, sa, sb, std::false_type{}, I0{});
             body(j + 1, sb, sa, std::false_type{}, I1{});
         }
-        for (; j < jfull; ++j) {
-            body_any(j, sa, sb, std::false_type{});
-            sa = sb;
+        // The rest (at most one unmasked block, then the diagonal and ragged
+        // ones) runs the masked body, whose tests are false on an unmasked
+        // block, also two blocks at a time: j is even here, so both stages
+        // stay compile-time and the score buffers alternate without copies.
+        // (One block at a time, with the stage chosen at run time and the
+        // scores copied back, made the register allocator copy the
+        // accumulators on every such block.)
+        for (; j + 1 < jhi; j += 2) {
+            body(j, sa, sb, std::true_type{}, I0{});
+            body(j + 1, sb, sa, std::true_type{}, I1{});
         }
-        for (; j < jhi; ++j) {
-            body_any(j, sa, sb, std::true_type{});
-            sa = sb;
-        }
+        if (j < jhi) body(j, sa, sb, std::true_type{}, I0{});
     } else if constexpr (D == 64) {
         // Block j sits in stage (j - jlo) % NS; the interior loop is unrolled
         // by NS so that stages are compile-time (immediate LDS offsets).
@@ -700,14 +699,10 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
             __syncthreads();                  // ... everyone's, and the stage of block j-1 is free
             issue(j + NS - 1, std::integral_constant<int, (S + NS - 1) % NS>{});
             const int kb = j * BK;
+            // masked blocks: no instruction moves between them (interleaving
+            // the unrolled masked blocks costs registers)
+            if constexpr (decltype(mask_tag)::value) __builtin_amdgcn_sched_barrier(0);
             if (!decltype(mask_tag)::value || !CAUSAL || kb <= wq_last + off) step(stage_tag, kb, mask_tag);
-        };
-        auto blk_any = [&](int j, auto mask_tag) {
-            switch ((j - jlo) % 3) {
-                case 0: blk(j, I0{}, mask_tag); break;
-                case 1: blk(j, I1{}, mask_tag); break;
-                default: blk(j, I2{}, mask_tag); break;
-            }
         };
         int j = jlo;
         const int jfull = min(nfull, jhi);
@@ -716,8 +711,18 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
             blk(j + 1, I1{}, std::false_type{});
             blk(j + 2, I2{}, std::false_type{});
         }
-        for (; j < jfull; ++j) blk_any(j, std::false_type{});
-        for (; j < jhi; ++j) blk_any(j, std::true_type{});
+        // The rest (at most two unmasked blocks, then the diagonal and ragged
+        // ones) runs the masked body, three blocks at a time from
+        // j - jlo = 0 mod 3, so stages stay compile-time.  (A stage chosen at
+        // run time made the register allocator copy the accumulators at the
+        // join on every such block.)
+        for (; j + 2 < jhi; j += 3) {
+            blk(j, I0{}, std::true_type{});
+            blk(j + 1, I1{}, std::true_type{});
+            blk(j + 2, I2{}, std::true_type{});
+        }
+        if (j < jhi) blk(j, I0{}, std::true_type{});
+        if (j + 1 < jhi) blk(j + 1, I1{}, std::true_type{});
     } else {
 #pragma unroll
     for (int j = 0; j < NS - 1; ++j) issue_rt(jlo + j);
