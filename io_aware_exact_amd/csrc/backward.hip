@@ -21,10 +21,14 @@
 // * bwd_dkdv: one workgroup per 128-key tile (32 keys per wave, one key per
 //   lane column).  K and V of the wave stay in VGPRs as MFMA B operands; Q and
 //   dO blocks (64 rows at d = 64, 32 at d = 128) and their row statistics
-//   stream through a 3-stage LDS ring filled by DMA.  Per block: S = Q K^T and dP = dO V^T (Q, dO read
-//   as rows), then dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T read by
-//   ds_read_b64_tr_b16, so P and dS go from the accumulator layout to the B
-//   operand with only a bf16 pack.
+//   stream through a 3-stage LDS ring filled by DMA.  Per block: S = Q K^T
+//   and dP = dO V^T (Q, dO read as rows), then dV^T += dO^T P and
+//   dK^T += Q^T dS with dO^T, Q^T read by ds_read_b64_tr_b16, so P and dS go
+//   from the accumulator layout to the B operand with only a bf16 pack.
+// Both kernels unroll their block loops by the ring depth, so every LDS read
+// is a per-lane address fixed before the loop plus a constant offset, and
+// no loop holds a branch that joins with the accumulators live (the register
+// allocator copies them at such joins).
 // Q and dO (in bwd_dkdv) and K (in bwd_dq) are read both as rows and
 // transposed, so their LDS chunk swizzle is conflict-free for both patterns.
 // Products are bf16 MFMA with fp32 accumulation; P and dS are rounded to
