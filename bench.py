@@ -715,7 +715,8 @@ def achievable_ceilings(torch):
 
 
 ISSUE_MODES = ("exp2_mul", "fma_mul", "mfma", "mfma_beside_exp2", "mfma_beside_fma", "prefill_block_mix",
-               "lds_read_b128", "lds_read_b64_tr_b16")
+               "lds_read_b128", "lds_read_b64_tr_b16", "exp2", "exp2_beside_fma", "fma32_mfma2", "fma32_mfma4",
+               "fma32_mfma16x16x32_4", "fma32")
 ISSUE_OPS = {"exp2_mul": 16, "fma_mul": 16, "mfma": 2}   # independent ops per loop iteration
 
 
@@ -729,8 +730,10 @@ def instruction_rates(torch, waves=(1, 2, 3), rounds: int = 8):
     at 3 waves per SIMD (the prefill kernels' occupancy): cycles per exp2+mul
     pair, per fma+mul pair, per 32x32x16 bf16 MFMA, the share of the
     prefill's per-block mix (16 MFMAs and the softmax of 32 scores per lane,
-    from registers) that the matrix pipe is busy, and the LDS read rate of a
-    compute unit (conflict-free ds_read_b128, and ds_read_b64_tr_b16).  None if the probe library is
+    from registers) that the matrix pipe is busy, the LDS read rate of a
+    compute unit (conflict-free ds_read_b128, and ds_read_b64_tr_b16), and
+    the issue-port time of an exp2, an FMA and each MFMA shape (what each
+    adds to a loop of 32 independent FMAs).  None if the probe library is
     not built."""
     import ctypes
 
@@ -785,6 +788,12 @@ def instruction_rates(torch, waves=(1, 2, 3), rounds: int = 8):
         # 4 SIMDs each finish one wave-iteration of 8 KiB of reads per that many cycles
         "lds_read_bytes_per_clk_per_cu": 4 * 8192 / cycles["lds_read_b128"][w3],
         "lds_read_tr_bytes_per_clk_per_cu": 4 * 8192 / cycles["lds_read_b64_tr_b16"][w3],
+        # issue-port time: what an instruction adds to 32 independent FMAs
+        "cycles_per_exp2": cycles["exp2"][w3] / 16,
+        "exp2_beside_16_fma_over_sum": cycles["exp2_beside_fma"][w3] / (cycles["exp2"][w3] + cycles["fma32"][w3] / 2),
+        "cycles_per_fma": cycles["fma32"][w3] / 32,
+        "port_cycles_per_mfma_32x32x16_bf16": (cycles["fma32_mfma4"][w3] - cycles["fma32"][w3]) / 4,
+        "port_cycles_per_mfma_16x16x32_bf16": (cycles["fma32_mfma16x16x32_4"][w3] - cycles["fma32"][w3]) / 4,
         "probe": ("instruction-mix probe (libattn_probe.so, issue_probe.hip): loops with no memory traffic, "
                   "w waves per SIMD held by an LDS reservation; modes " + ", ".join(ISSUE_MODES)),
     }

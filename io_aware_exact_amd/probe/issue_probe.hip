@@ -24,6 +24,13 @@
 //   7  the same 8 KiB per wave as 16 ds_read_b64_tr_b16: the transposing
 //      read, with the head-width-64 prefill's V operand addressing (a 64-row
 //      tile of 128-byte rows, 16-byte chunks XOR-swizzled by row bit 1)
+// Issue-port cost (each against mode 13):
+//   8  16 independent v_exp_f32                  transcendental rate alone
+//   9  mode 8 beside 16 independent v_fma_f32    does the exp share the port
+//  10  32 independent v_fma_f32 beside 2 v_mfma_f32_32x32x16_bf16
+//  11  the same beside 4 of them                 port time per 32x32x16 MFMA
+//  12  the same beside 4 v_mfma_f32_16x16x32_bf16 (half the flops each)
+//  13  32 independent v_fma_f32                  the VALU baseline
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -37,6 +44,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -81,7 +89,11 @@ void issue_probe_kernel(int iters, const u32x4_t* __restrict__ operands, float* 
     float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] = -1e-3f * (float)(tid + i);
-    f32x16_t c0 = {}, c1 = {};
+    f32x16_t c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    f32x4_t e0 = {}, e1 = {}, e2 = {}, e3 = {};
+    float y[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) y[i] = 2e-3f * (float)(tid + 2 * i);
     float m = 0.5f, l = 0.f;
     const float c = 0.18f;
     const long long r0 = __builtin_amdgcn_s_memrealtime();
@@ -135,6 +147,32 @@ void issue_probe_kernel(int iters, const u32x4_t* __restrict__ operands, float* 
         } else if constexpr (MODE == 2) {
             c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[0], q[0], c0, 0, 0, 0);
             c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[1], q[1], c1, 0, 0, 0);
+        } else if constexpr (MODE == 8 || MODE == 9) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                x[i] = __builtin_amdgcn_exp2f(-x[i]);
+                if constexpr (MODE == 9) y[i] = __builtin_fmaf(y[i], 0.999f, 1e-4f);
+            }
+        } else if constexpr (MODE >= 10 && MODE <= 13) {
+            if constexpr (MODE == 10 || MODE == 11) {
+                c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[0], q[0], c0, 0, 0, 0);
+                c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[1], q[1], c1, 0, 0, 0);
+            }
+            if constexpr (MODE == 11) {
+                c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[2], q[2], c2, 0, 0, 0);
+                c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k[3], q[3], c3, 0, 0, 0);
+            }
+            if constexpr (MODE == 12) {
+                e0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k[0], q[0], e0, 0, 0, 0);
+                e1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k[1], q[1], e1, 0, 0, 0);
+                e2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k[2], q[2], e2, 0, 0, 0);
+                e3 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k[3], q[3], e3, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                x[i] = __builtin_fmaf(x[i], 0.999f, 1e-4f);
+                y[i] = __builtin_fmaf(y[i], 0.999f, 1e-4f);
+            }
         } else {   // 5
             asm volatile("" : "+v"(k[0]), "+v"(k[4]));   // opaque every iteration: nothing is hoisted
             f32x16_t s0 = {}, s1 = {};
@@ -172,7 +210,9 @@ void issue_probe_kernel(int iters, const u32x4_t* __restrict__ operands, float* 
     const long long r1 = __builtin_amdgcn_s_memrealtime();
     float sum = l + m;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sum += x[i] + c0[i] + c1[i];
+    for (int i = 0; i < 16; ++i) sum += x[i] + y[i] + c0[i] + c1[i] + c2[i] + c3[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sum += e0[i] + e1[i] + e2[i] + e3[i];
     out[(size_t)blockIdx.x * kThreads + tid] = sum;
     if ((tid & 63) == 0) {
         const size_t w = (size_t)blockIdx.x * (kThreads / 64) + (tid >> 6);
@@ -199,7 +239,7 @@ extern "C" {
 
 // Number of modes, and the bf16x8 operand words the caller provides
 // (20 per lane of a wave: 20 * 64 * 16 bytes).
-int probe_issue_modes(void) { return 8; }
+int probe_issue_modes(void) { return 14; }
 int probe_issue_operand_bytes(void) { return 20 * 64 * 16; }
 int probe_issue_threads(void) { return kThreads; }
 
@@ -211,7 +251,7 @@ int probe_issue_threads(void) { return kThreads; }
 // hipError_t of the launch; invalid arguments are refused before any launch.
 int probe_issue(int mode, int waves, int blocks, int iters, const void* operands, float* out, long long* ticks,
                 hipStream_t stream) {
-    if (mode < 0 || mode > 7 || waves < 1 || waves > 3 || blocks < 1 || iters < 1 || !operands || !out || !ticks)
+    if (mode < 0 || mode > 13 || waves < 1 || waves > 3 || blocks < 1 || iters < 1 || !operands || !out || !ticks)
         return (int)hipErrorInvalidValue;
     const u32x4_t* ops = static_cast<const u32x4_t*>(operands);
     switch (mode) {
@@ -222,7 +262,13 @@ int probe_issue(int mode, int waves, int blocks, int iters, const void* operands
         case 4: return (int)launch_mode<4>(waves, blocks, iters, ops, out, ticks, stream);
         case 5: return (int)launch_mode<5>(waves, blocks, iters, ops, out, ticks, stream);
         case 6: return (int)launch_mode<6>(waves, blocks, iters, ops, out, ticks, stream);
-        default: return (int)launch_mode<7>(waves, blocks, iters, ops, out, ticks, stream);
+        case 7: return (int)launch_mode<7>(waves, blocks, iters, ops, out, ticks, stream);
+        case 8: return (int)launch_mode<8>(waves, blocks, iters, ops, out, ticks, stream);
+        case 9: return (int)launch_mode<9>(waves, blocks, iters, ops, out, ticks, stream);
+        case 10: return (int)launch_mode<10>(waves, blocks, iters, ops, out, ticks, stream);
+        case 11: return (int)launch_mode<11>(waves, blocks, iters, ops, out, ticks, stream);
+        case 12: return (int)launch_mode<12>(waves, blocks, iters, ops, out, ticks, stream);
+        default: return (int)launch_mode<13>(waves, blocks, iters, ops, out, ticks, stream);
     }
 }
 
