@@ -81,6 +81,7 @@ CASES = [
     (1, 1, 300, 17, False),     # fewer keys than a key tile
     (2, 2, 64, 64, True),
     (1, 1, 1, 50, False),       # a single query
+    (1, 2, 449, 449, True),     # 1-8 blocks per tile: every remainder of the unrolled loops
 ]
 
 

@@ -233,6 +233,11 @@ D64_PATH_CASES = [
     (2, 24, 1100, 1300, True, True, False),
     (3, 5, 333, 333, False, True, False),
     (1, 1, 65, 65, True, True, False),
+    # 449 rows: tiles of 1-8 key blocks, so the unrolled loops end with every
+    # remainder of unmasked and masked blocks
+    (1, 192, 449, 449, True, False, False),
+    (1, 192, 449, 449, False, False, False),
+    (1, 2, 449, 449, True, True, False),
     (4, 100, 129, 200, False, False, True),
     (3, 131, 250, 77, False, False, True),
     (1, 200, 500, 500, False, False, True),
