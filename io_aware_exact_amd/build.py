@@ -30,12 +30,14 @@ PROBE_LIB = os.path.join(PKG, "libattn_probe.so")
 ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
-# Per-source device flags.  The backward kernels are scheduled for
-# instruction-level parallelism rather than occupancy (their register budget
-# is set by their launch bounds either way): measured 2 % faster on the
-# gpt2-shaped backward, 1 % slower on its head-width-128 form; the forward
-# kernels lose with it (the head-width-128 prefill by 3 %).
-SOURCE_DEVICE_FLAGS = {"backward.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+# Per-source device flags.  The backward kernels and the VALU decode kernel
+# are scheduled for instruction-level parallelism rather than occupancy (their
+# register budgets are set by their launch bounds either way): measured 2 %
+# faster on the gpt2-shaped backward (1 % slower on its head-width-128 form)
+# and 1.5 % on the split-KV decode steps; the forward kernels and the
+# matrix-core decode lose with it (the head-width-128 prefill by 3 %).
+ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
+SOURCE_DEVICE_FLAGS = {"backward.hip": ILP, "decode.hip": ILP}
 
 
 def hipcc() -> str:

@@ -68,6 +68,10 @@ size_t backward_workspace_bytes(int B, int H, int Tq);
 hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream, const char** name);
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream, const char** name);
+// (decode_mfma.hip) grouped-query decode on the matrix cores, groups of 4 and more
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream, const char** name);
+// (decode.hip) the merge of a.num_splits partial records per query head
+hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream);
 int decode_auto_splits(int B, int Hq, int Hkv, int Tkv, int d);
 
 // Size of the library's own per-device decode partials (32 MiB), and its
