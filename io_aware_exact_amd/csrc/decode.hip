@@ -65,19 +65,18 @@ void decode_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
                          uint16_t* __restrict__ O, float* __restrict__ LSE,
                          int Hkv, int G, int Tkv, int P, float c, int direct) {
     using S = DecodeShape<D, GT>;
-    constexpr int LPK = S::LPK, KPW = S::KPW, GROUPS = S::GROUPS, UNROLL = S::UNROLL, STEP = S::STEP;
+    constexpr int LPK = S::LPK, KPW = S::KPW, UNROLL = S::UNROLL, STEP = S::STEP;
     constexpr int HP = S::HP;
 
-    __shared__ float red_o[HP][GROUPS][D];
-    __shared__ float red_m[HP][GROUPS];
-    __shared__ float red_l[HP][GROUPS];
+    __shared__ float red_o[HP][NW][D];
+    __shared__ float red_m[HP][NW];
+    __shared__ float red_l[HP][NW];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int kr = lane / LPK;         // key slot inside one wave load
     const int dc = lane % LPK;         // which 8 elements of the row
-    const int grp = wave * KPW + kr;   // softmax-state group
 
     // blockIdx.x = (b * Hkv + hk) * (G / GT) + tile
     const int tiles = G / GT;
@@ -168,17 +167,35 @@ void decode_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
         }
     }
 
-    // ---- merge the GROUPS states of this workgroup, HP heads per LDS pass ----
+    // ---- merge the GROUPS states of this workgroup: first the KPW groups of
+    // each wave across lanes (lane bits above the row's LPK lanes), then the
+    // NW waves through LDS, HP heads per LDS pass ----
+#pragma unroll
+    for (int x = LPK; x < 64; x <<= 1) {
+#pragma unroll
+        for (int t = 0; t < GT; ++t) {
+            const float mo = __shfl_xor(m[t], x), lo = __shfl_xor(l[t], x);
+            const float mm = fmaxf(m[t], mo);
+            const float mu = (mm == kNegInf) ? 0.f : mm;
+            const float wa = fast_exp2(m[t] - mu), wb = fast_exp2(mo - mu);
+            l[t] = wa * l[t] + wb * lo;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[t][i] = wa * o[t][i] + wb * __shfl_xor(o[t][i], x);
+            m[t] = mm;
+        }
+    }
 #pragma unroll
     for (int t0 = 0; t0 < GT; t0 += HP) {
         if (t0 > 0) __syncthreads();   // the previous pass has finished reading
+        if (kr == 0) {
 #pragma unroll
-        for (int t = 0; t < HP; ++t) {
+            for (int t = 0; t < HP; ++t) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) red_o[t][grp][8 * dc + i] = o[t0 + t][i];
-            if (dc == 0) {
-                red_m[t][grp] = m[t0 + t];
-                red_l[t][grp] = l[t0 + t];
+                for (int i = 0; i < 8; ++i) red_o[t][wave][8 * dc + i] = o[t0 + t][i];
+                if (dc == 0) {
+                    red_m[t][wave] = m[t0 + t];
+                    red_l[t][wave] = l[t0 + t];
+                }
             }
         }
         __syncthreads();
@@ -186,10 +203,12 @@ void decode_split_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restr
             const int t = e / D;
             const int d = e - t * D;
             float M = kNegInf;
-            for (int g = 0; g < GROUPS; ++g) M = fmaxf(M, red_m[t][g]);
+#pragma unroll
+            for (int g = 0; g < NW; ++g) M = fmaxf(M, red_m[t][g]);
             const float Mu = (M == kNegInf) ? 0.f : M;
             float L = 0.f, acc = 0.f;
-            for (int g = 0; g < GROUPS; ++g) {
+#pragma unroll
+            for (int g = 0; g < NW; ++g) {
                 const float w = fast_exp2(red_m[t][g] - Mu);
                 L += w * red_l[t][g];
                 acc += w * red_o[t][g][d];
